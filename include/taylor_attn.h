@@ -1,0 +1,152 @@
+/*
+ * taylor_attn.h -- C ABI of the MI355X (gfx950) causal Taylor-series linear
+ * attention library (libtaylor_attn.so).
+ *
+ * What is computed. For one (batch, head) with queries q_t, keys k_s in R^d
+ * and values v_s in R^dv, t = 0..N-1, and n = n_terms:
+ *
+ *   w(x)  = sum_{m=0}^{n-1} x^m / m!            (truncated exp; coefficient
+ *                                               1/(m! a^m) on (q.k)^m)
+ *   o_t   = sum_{s<=t} w(q_t.k_s / a) v_s  /  sum_{s<=t} w(q_t.k_s / a)
+ *
+ * ("Expanding Attention: A Taylor-Series Route to Linear-Time Transformers
+ * with a Fixed Number of Recurrent States": the expansion of exp(q.k/a),
+ * the causal mask and normalisation of the softmax it replaces.) The library
+ * evaluates it through per-order states (same page, "Memory"; the
+ * linear-attention recurrence S_t = S_{t-1} + v_t phi(k_t)^T of the Spanish
+ * linear-attention explainer):
+ *
+ *   S_m = sum_s phi_m(k_s) v_s^T   [F_m x dv],   z_m = sum_s phi_m(k_s)   [F_m]
+ *   o_t = sum_m alpha_m phi_m(q_t)^T S_m / sum_m alpha_m phi_m(q_t)^T z_m,
+ *   alpha_m = 1 / (m! a^m),
+ *
+ * where phi_m is the symmetric tensor-power feature map of width
+ * F_m = C(d+m-1, m) ("Higher orders"): one feature per index tuple
+ * i_1 <= ... <= i_m, value sqrt(m! / prod_i c_i!) * prod_j x[i_j] (c_i counts
+ * index i in the tuple), so phi_m(x).phi_m(y) = (x.y)^m.
+ *
+ * Canonical feature order (the F axis of every state buffer): orders
+ * m = 0..n-1 ascending; within order m, tuples in lexicographic order.
+ * F = sum_m F_m = C(d+n-1, n-1).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller, dense row-major, with the layouts stated per argument. The
+ *    library allocates no device memory and never synchronises: work is
+ *    enqueued on `stream` (a hipStream_t passed as void*; NULL = the default
+ *    stream) and kernel errors surface at the caller's next synchronisation.
+ *  - Argument checks are synchronous and happen before anything is enqueued;
+ *    on a non-OK status nothing has been launched and no output is touched.
+ *  - Inputs are not scanned for NaN or Inf; such values propagate.
+ *  - taylor_last_error() returns a message for the last non-OK status on the
+ *    calling thread (thread-local; valid until the next call on that thread).
+ *  - Supported (d, dv, n_terms): d = 16 with dv in {16, 64} and n_terms in
+ *    {1, 3, 5}; d = 64 with dv in {16, 64} and n_terms in {1, 3}. n_terms must
+ *    be odd so that the highest order is even and every weight is positive
+ *    ("Two prerequisites" on the same page; posfloor README, "The 1/2
+ *    positivity floor": even truncations are globally positive). Anything
+ *    else returns TAYLOR_ERR_UNSUPPORTED.
+ */
+#ifndef TAYLOR_ATTN_H
+#define TAYLOR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TAYLOR_OK = 0,
+  TAYLOR_ERR_NULL_PTR = 1,    /* a required pointer is NULL, or only one of a pointer pair is */
+  TAYLOR_ERR_BAD_SHAPE = 2,   /* negative size, or a size product overflowing int64 */
+  TAYLOR_ERR_UNSUPPORTED = 3, /* (d, dv, n_terms) or dtype not instantiated; even n_terms */
+  TAYLOR_ERR_BAD_SCALE = 4,   /* a not finite or a <= 0 */
+  TAYLOR_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the size query returned */
+  TAYLOR_ERR_HIP = 6          /* a HIP launch failed (message from hipGetErrorString) */
+} taylor_status;
+
+typedef enum {
+  TAYLOR_F32 = 0,  /* IEEE binary32 */
+  TAYLOR_BF16 = 1  /* bfloat16 (upper half of binary32) */
+} taylor_dtype;
+
+/* Width F = sum_{m<n} C(d+m-1, m) of the symmetric basis; -1 if d < 1,
+ * n_terms < 1 or the result overflows int64. Pure host function. */
+int64_t taylor_feature_dim(int d, int n_terms);
+
+/* 1 if (d, dv, n_terms) is an instantiated configuration, else 0. */
+int taylor_is_supported(int d, int dv, int n_terms);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* taylor_last_error(void);
+
+/*
+ * Symmetric feature map (the basis above).
+ *   x    [rows, d]  x_dtype (F32 or BF16), device.
+ *   phi  [rows, F]  float32, device, written in full.
+ *   fold_alpha = 0: block m holds phi_m(x), so phi_m(x).phi_m(y) = (x.y)^m.
+ *   fold_alpha = 1: block m is also scaled by sqrt(alpha_m) = (m! a^m)^(-1/2),
+ *                   so phi(x).phi(y) = w(x.y / a).  `a` is ignored when 0.
+ * rows = 0 is valid and launches nothing. Same (d, n_terms) support set as the
+ * attention calls (dv is not involved).
+ */
+taylor_status taylor_feature_map(const void* x, taylor_dtype x_dtype, int64_t rows, int d,
+                                 int n_terms, float a, int fold_alpha, float* phi,
+                                 void* stream);
+
+/*
+ * Bytes of device workspace taylor_attn_prefill needs for these sizes (0 if
+ * none). Depends only on the arguments, and is the same for any output dtype.
+ * Returns (size_t)-1 when the arguments would be rejected by the call.
+ */
+size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_terms,
+                                     taylor_dtype in_dtype);
+
+/*
+ * Causal prefill over N tokens for B x H independent heads.
+ *   q, k      [B, H, N, d]   in_dtype (F32 or BF16)
+ *   v         [B, H, N, dv]  in_dtype
+ *   S0, z0    [B, H, F, dv], [B, H, F] float32: state of earlier tokens to
+ *             continue from (both NULL = start from zero). States are
+ *             additive (the closing paragraph of the same page), so
+ *             prefill(x1) then prefill(x2 | S, z) equals prefill(x1 ++ x2).
+ *   o         [B, H, N, dv]  out_dtype (F32 or BF16), or NULL to compute the
+ *             state only.
+ *   S, z      [B, H, F, dv], [B, H, F] float32: final state after the N
+ *             tokens (both NULL = not wanted). S may be the same buffer as
+ *             S0 and z the same as z0 (in-place continuation); other
+ *             overlaps between inputs and outputs are not allowed.
+ *   workspace at least taylor_attn_prefill_workspace(...) bytes of device
+ *             memory (may be NULL when that size is 0). Its contents are
+ *             scratch: clobbered by the call, never read before written.
+ * B, H or N may be 0: then no token is processed; with N = 0 the final state
+ * is S0 (or zero). The normalisation divides by a sum of weights that is
+ * >= 1/2 per key for n_terms = 3 (>= 0.27 for 5), so it never divides by 0.
+ */
+taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
+                                  taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                  int n_terms, float a, const float* S0, const float* z0,
+                                  void* o, taylor_dtype out_dtype, float* S, float* z,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * One generation step for B x H heads: update the state with (k, v), then
+ * read out with q (update before read-out, as in S_t = S_{t-1} + v_t phi(k_t)^T,
+ * o_t = S_t phi(q_t)).
+ *   q, k  [B, H, d]   in_dtype;  v [B, H, dv]  in_dtype
+ *   S, z  [B, H, F, dv], [B, H, F] float32, read and updated in place.
+ *   o     [B, H, dv]  out_dtype.
+ * B or H may be 0 (nothing launched).
+ */
+taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
+                                 taylor_dtype in_dtype, int B, int H, int d, int dv,
+                                 int n_terms, float a, float* S, float* z, void* o,
+                                 taylor_dtype out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAYLOR_ATTN_H */

@@ -1,0 +1,272 @@
+// C ABI of libtaylor_attn.so: argument checks, segment planning, dispatch.
+// The operation itself is documented in include/taylor_attn.h.
+#include "../../include/taylor_attn.h"
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "features.hpp"
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+taylor_status fail(taylor_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool supported(int d, int dv, int n_terms) {
+  if (dv != 16 && dv != 64) return false;
+  if (d == 16) return n_terms == 1 || n_terms == 3 || n_terms == 5;
+  if (d == 64) return n_terms == 1 || n_terms == 3;
+  return false;
+}
+
+bool supported_dn(int d, int n_terms) { return supported(d, 16, n_terms); }
+
+taylor_status check_dn(int d, int dv, int n_terms, bool with_dv) {
+  if (n_terms >= 1 && n_terms % 2 == 0)
+    return fail(TAYLOR_ERR_UNSUPPORTED,
+                "n_terms must be odd (highest order even, so every weight is positive); got " +
+                    std::to_string(n_terms));
+  if (with_dv ? !supported(d, dv, n_terms) : !supported_dn(d, n_terms))
+    return fail(TAYLOR_ERR_UNSUPPORTED,
+                "unsupported configuration d=" + std::to_string(d) +
+                    (with_dv ? " dv=" + std::to_string(dv) : std::string()) +
+                    " n_terms=" + std::to_string(n_terms) +
+                    " (supported: d=16 with n_terms 1,3,5; d=64 with n_terms 1,3; dv 16 or 64)");
+  return TAYLOR_OK;
+}
+
+taylor_status check_scale(float a) {
+  if (!std::isfinite(a) || !(a > 0.f))
+    return fail(TAYLOR_ERR_BAD_SCALE, "scale a must be finite and > 0");
+  return TAYLOR_OK;
+}
+
+taylor_status check_dtype(taylor_dtype t, const char* what) {
+  if (t != TAYLOR_F32 && t != TAYLOR_BF16)
+    return fail(TAYLOR_ERR_UNSUPPORTED, std::string(what) + " must be TAYLOR_F32 or TAYLOR_BF16");
+  return TAYLOR_OK;
+}
+
+// a*b*c*... without int64 overflow; -1 on overflow or negative input.
+int64_t checked_mul(std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && r > INT64_MAX / x) return -1;
+    r *= x;
+  }
+  return r;
+}
+
+struct Plan {
+  tl::PrefillTraits t;
+  int P = 1;
+  int L = 0;
+  size_t seg_off = 0, fin_off = 0, part_off = 0, bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Sequence split: enough workgroups (heads x segments x slices) to give each
+// compute unit about two, and at least 4 chunks per segment.
+void plan_prefill(int BH, int N, int dv, const tl::PrefillTraits& t, Plan* p) {
+  p->t = t;
+  const int C = t.C;
+  const int64_t nchunks = (static_cast<int64_t>(N) + C - 1) / C;
+  if (BH <= 0 || nchunks == 0) {
+    p->P = 1;
+    p->L = N;
+    p->bytes = 0;
+    return;
+  }
+  const int64_t target = 512;
+  int64_t want = (target + static_cast<int64_t>(BH) * t.G - 1) / (static_cast<int64_t>(BH) * t.G);
+  int64_t maxp = nchunks / 4 > 1 ? nchunks / 4 : 1;
+  int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
+  const int64_t cps = (nchunks + P - 1) / P;
+  p->L = static_cast<int>(cps * C);
+  p->P = static_cast<int>((nchunks + cps - 1) / cps);
+  const int DVP = t.NW * 16;
+  const size_t FP = static_cast<size_t>(t.G) * t.FS;
+  size_t off = 0;
+  p->seg_off = off;
+  if (p->P > 1) off += align256(static_cast<size_t>(BH) * (p->P - 1) * FP * DVP * 4);
+  p->fin_off = off;
+  if (p->P > 1) off += align256(static_cast<size_t>(BH) * FP * DVP * 4);
+  p->part_off = off;
+  if (t.G > 1) off += align256(static_cast<size_t>(t.G) * BH * static_cast<size_t>(N) * (dv + 4) * 4);
+  p->bytes = off;
+}
+
+taylor_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return TAYLOR_OK;
+  return fail(TAYLOR_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// Validation shared by the size query and the call.
+taylor_status check_prefill_shape(int B, int H, int N, int d, int dv, int n_terms,
+                                  taylor_dtype in_dtype, tl::PrefillTraits* t) {
+  taylor_status s = check_dtype(in_dtype, "in_dtype");
+  if (s != TAYLOR_OK) return s;
+  if (B < 0 || H < 0 || N < 0)
+    return fail(TAYLOR_ERR_BAD_SHAPE, "B, H and N must be >= 0");
+  if ((s = check_dn(d, dv, n_terms, true)) != TAYLOR_OK) return s;
+  if (checked_mul({B, H, N, d > dv ? d : dv}) < 0 || checked_mul({B, H}) > INT32_MAX / 64)
+    return fail(TAYLOR_ERR_BAD_SHAPE, "B*H*N*max(d,dv) overflows");
+  if (!tl::prefill_traits(d, dv, n_terms, in_dtype == TAYLOR_BF16, t))
+    return fail(TAYLOR_ERR_UNSUPPORTED, "no prefill instantiation for this configuration");
+  return TAYLOR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t taylor_feature_dim(int d, int n_terms) {
+  if (d < 1 || n_terms < 1) return -1;
+  // C(d+n-1, n-1) computed incrementally with an overflow guard
+  long double f = 0;
+  int64_t total = 0;
+  for (int m = 0; m < n_terms; ++m) {
+    // C(d+m-1, m)
+    long double c = 1;
+    for (int i = 1; i <= m; ++i) c = c * (d - 1 + i) / i;
+    f += c;
+    if (f > static_cast<long double>(INT64_MAX) / 2) return -1;
+  }
+  total = static_cast<int64_t>(std::llround(static_cast<double>(f)));
+  return total;
+}
+
+int taylor_is_supported(int d, int dv, int n_terms) { return supported(d, dv, n_terms) ? 1 : 0; }
+
+const char* taylor_last_error(void) { return g_last_error.c_str(); }
+
+taylor_status taylor_feature_map(const void* x, taylor_dtype x_dtype, int64_t rows, int d,
+                                 int n_terms, float a, int fold_alpha, float* phi,
+                                 void* stream) {
+  taylor_status s = check_dtype(x_dtype, "x_dtype");
+  if (s != TAYLOR_OK) return s;
+  if (rows < 0) return fail(TAYLOR_ERR_BAD_SHAPE, "rows must be >= 0");
+  if ((s = check_dn(d, 16, n_terms, false)) != TAYLOR_OK) return s;
+  if (fold_alpha && (s = check_scale(a)) != TAYLOR_OK) return s;
+  const int F = tl::feature_count(d, n_terms);
+  if (checked_mul({rows, F}) < 0 || checked_mul({rows, d}) < 0)
+    return fail(TAYLOR_ERR_BAD_SHAPE, "rows*F overflows");
+  if (rows == 0) return TAYLOR_OK;
+  if (x == nullptr || phi == nullptr) return fail(TAYLOR_ERR_NULL_PTR, "x and phi are required");
+  tl::OrderScale sc{};
+  for (int m = 0; m < 8; ++m) {
+    double v = 1.0;
+    if (fold_alpha) v = 1.0 / std::sqrt(static_cast<double>(tl::factorial(m)) * std::pow(static_cast<double>(a), m));
+    sc.s[m] = static_cast<float>(v);
+  }
+  return hip_status(tl::feature_map_launch(d, n_terms, x_dtype == TAYLOR_BF16, x, rows, phi, sc,
+                                           static_cast<hipStream_t>(stream)),
+                    "taylor_feature_map launch");
+}
+
+size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_terms,
+                                     taylor_dtype in_dtype) {
+  tl::PrefillTraits t;
+  if (check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &t) != TAYLOR_OK) return static_cast<size_t>(-1);
+  Plan p;
+  plan_prefill(B * H, N, dv, t, &p);
+  return p.bytes;
+}
+
+taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
+                                  taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                  int n_terms, float a, const float* S0, const float* z0,
+                                  void* o, taylor_dtype out_dtype, float* S, float* z,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  tl::PrefillTraits t;
+  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &t);
+  if (s != TAYLOR_OK) return s;
+  if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
+  if ((s = check_scale(a)) != TAYLOR_OK) return s;
+  if ((S0 == nullptr) != (z0 == nullptr))
+    return fail(TAYLOR_ERR_NULL_PTR, "S0 and z0 must both be given or both be NULL");
+  if ((S == nullptr) != (z == nullptr))
+    return fail(TAYLOR_ERR_NULL_PTR, "S and z must both be given or both be NULL");
+  const int BH = B * H;
+  if (BH > 0 && N > 0 && (q == nullptr || k == nullptr || v == nullptr))
+    return fail(TAYLOR_ERR_NULL_PTR, "q, k and v are required");
+  Plan p;
+  plan_prefill(BH, N, dv, t, &p);
+  if (p.bytes > 0 && (workspace == nullptr || ws_bytes < p.bytes))
+    return fail(TAYLOR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.bytes) +
+                                          " bytes, got " + std::to_string(ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (BH == 0) return TAYLOR_OK;
+  (void)hipGetLastError();  // report only errors of the launches below
+  if (N == 0) {
+    if (S == nullptr) return TAYLOR_OK;
+    return hip_status(tl::state_init_launch(S0, z0, S, z, BH, t.F, dv, st), "state init launch");
+  }
+  tl::PrefillArgs args{};
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.S0 = S0;
+  args.z0 = z0;
+  args.o = o;
+  args.out_bf16 = out_dtype == TAYLOR_BF16;
+  args.S = S;
+  args.z = z;
+  char* ws = static_cast<char*>(workspace);
+  args.seg = p.P > 1 ? reinterpret_cast<float*>(ws + p.seg_off) : nullptr;
+  args.fin = p.P > 1 ? reinterpret_cast<float*>(ws + p.fin_off) : nullptr;
+  args.part = t.G > 1 ? reinterpret_cast<float*>(ws + p.part_off) : nullptr;
+  args.BH = BH;
+  args.N = N;
+  args.P = p.P;
+  args.L = p.L;
+  args.inv_a = 1.0f / a;
+  // In-place continuation with several segments: the first segment reads S0
+  // while the last one finishes the state, so the final state goes through
+  // the workspace and is copied out afterwards.
+  args.defer_state = (S != nullptr && p.P > 1 && (S == S0 || z == z0)) ? 1 : 0;
+  return hip_status(tl::prefill_launch(d, dv, n_terms, in_dtype == TAYLOR_BF16, args, st),
+                    "taylor_attn_prefill launch");
+}
+
+taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
+                                 taylor_dtype in_dtype, int B, int H, int d, int dv,
+                                 int n_terms, float a, float* S, float* z, void* o,
+                                 taylor_dtype out_dtype, void* stream) {
+  taylor_status s = check_dtype(in_dtype, "in_dtype");
+  if (s != TAYLOR_OK) return s;
+  if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
+  if (B < 0 || H < 0) return fail(TAYLOR_ERR_BAD_SHAPE, "B and H must be >= 0");
+  if ((s = check_dn(d, dv, n_terms, true)) != TAYLOR_OK) return s;
+  if ((s = check_scale(a)) != TAYLOR_OK) return s;
+  if (checked_mul({B, H}) > INT32_MAX)
+    return fail(TAYLOR_ERR_BAD_SHAPE, "B*H exceeds the grid limit");
+  const int BH = B * H;
+  if (BH == 0) return TAYLOR_OK;
+  if (!q || !k || !v || !S || !z || !o)
+    return fail(TAYLOR_ERR_NULL_PTR, "q, k, v, S, z and o are required");
+  tl::DecodeArgs args{};
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.S = S;
+  args.z = z;
+  args.o = o;
+  args.out_bf16 = out_dtype == TAYLOR_BF16;
+  args.BH = BH;
+  args.inv_a = 1.0f / a;
+  (void)hipGetLastError();
+  return hip_status(tl::decode_launch(d, dv, n_terms, in_dtype == TAYLOR_BF16, args,
+                                      static_cast<hipStream_t>(stream)),
+                    "taylor_attn_decode launch");
+}
+
+}  // extern "C"

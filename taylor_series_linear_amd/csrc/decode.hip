@@ -1,0 +1,196 @@
+// Single-token decode step and the standalone feature map.
+//
+// Decode ("Expanding Attention: A Taylor-Series Route to Linear-Time
+// Transformers with a Fixed Number of Recurrent States", "Decoding": one
+// token costs sum_m C(d+m-1,m)(dv+1), independent of the context length):
+//   S_m += phi_m(k) v^T,  z_m += phi_m(k)      (update first ...)
+//   o = sum_m alpha_m phi_m(q)^T S_m / sum_m alpha_m phi_m(q)^T z_m  (... then read out)
+// following the linear-attention recurrence S_t = S_{t-1} + v_t phi(k_t)^T,
+// o_t = S_t phi(q_t) (Spanish linear-attention explainer).
+//
+// The step streams each head's state once: read, add, write back, and fold
+// the new row into the read-out while it is still in registers. It is bound
+// by HBM bandwidth (about 0.5 flop per state byte), so the kernel is shaped
+// for coalescing: 16 lanes cover one 64-float state row with 16-byte
+// accesses, every lane keeps several rows in flight, and the per-feature
+// weights phi(k), alpha*phi(q) are computed once per head into LDS.
+#include "features.hpp"
+#include "internal.hpp"
+#include "mma.hpp"
+
+namespace tl {
+
+template <int D, int NT>
+__device__ const PackedTable<D, NT> g_dtab = make_packed<D, NT>();
+
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void* p, size_t i) {
+  if constexpr (BF16)
+    return static_cast<float>(reinterpret_cast<const __bf16*>(p)[i]);
+  else
+    return reinterpret_cast<const float*>(p)[i];
+}
+
+template <int D, int DV, int NT, bool BF16>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  constexpr int F = feature_count(D, NT);
+  constexpr int NQ = DV / 4;         // float4 columns per state row
+  constexpr int NG = 256 / NQ;       // row groups
+  constexpr int RPT = (F + NG - 1) / NG;  // rows per thread (upper bound)
+  constexpr int BATCH = RPT < 8 ? RPT : 8;
+
+  __shared__ float sq[D], sk[D];
+  __shared__ __attribute__((aligned(16))) float sv[DV];
+  __shared__ float sfk[F], sfq[F];
+  __shared__ f32x4 red[256];
+  __shared__ float dred[256];
+
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const float inv_a = a.inv_a;
+
+  if (tid < D) {
+    sq[tid] = load_in<BF16>(a.q, static_cast<size_t>(bh) * D + tid);
+    sk[tid] = load_in<BF16>(a.k, static_cast<size_t>(bh) * D + tid);
+  }
+  if (tid < DV) sv[tid] = load_in<BF16>(a.v, static_cast<size_t>(bh) * DV + tid);
+  __syncthreads();
+
+  const auto& tab = g_dtab<D, NT>;
+  for (int f = tid; f < F; f += 256) {
+    const PackedFeature e = tab.e[f];
+    const int m = static_cast<int>(e.m);
+    float pk = e.w, pq = e.w * e.inv_mfact;
+    for (int j = 0; j < m; ++j) {
+      const int i = (e.idx >> (8 * j)) & 255;
+      pk *= sk[i];
+      pq *= sq[i] * inv_a;
+    }
+    sfk[f] = pk;
+    sfq[f] = pq;
+  }
+  __syncthreads();
+
+  const int dq = tid % NQ;
+  const int rg = tid / NQ;
+  float* Sh = a.S + static_cast<size_t>(bh) * F * DV;
+  const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * dq);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < RPT; r0 += BATCH) {
+    f32x4 rows[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int f = rg + NG * (r0 + j);
+      if (r0 + j < RPT && f < F) rows[j] = *reinterpret_cast<const f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq);
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int f = rg + NG * (r0 + j);
+      if (r0 + j < RPT && f < F) {
+        const f32x4 s = rows[j] + sfk[f] * vv;
+        *reinterpret_cast<f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq) = s;
+        acc += sfq[f] * s;
+      }
+    }
+  }
+  float dpart = 0.f;
+  float* zh = a.z + static_cast<size_t>(bh) * F;
+  for (int f = tid; f < F; f += 256) {
+    const float zz = zh[f] + sfk[f];
+    zh[f] = zz;
+    dpart += sfq[f] * zz;
+  }
+  red[tid] = acc;
+  dred[tid] = dpart;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) dred[tid] += dred[tid + s];
+    __syncthreads();
+  }
+  if (tid < NQ) {
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) num += red[g * NQ + tid];
+    const float r = 1.f / dred[0];
+    const size_t off = static_cast<size_t>(bh) * DV + 4 * tid;
+    if (a.out_bf16) {
+      bf16x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(num[i] * r);
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = num * r;
+    }
+  }
+}
+
+// phi[row, f] = w_f * prod_j x[row, i_j] * scale[m_f]
+template <int D, int NT, bool BF16>
+__global__ __launch_bounds__(256) void feature_map_kernel(const void* x, int64_t rows, float* phi,
+                                                          OrderScale sc) {
+  constexpr int F = feature_count(D, NT);
+  const auto& tab = g_dtab<D, NT>;
+  const int64_t total = rows * F;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = e / F;
+    const int f = static_cast<int>(e - r * F);
+    const PackedFeature pf = tab.e[f];
+    const int m = static_cast<int>(pf.m);
+    float v = pf.w * sc.s[m];
+    for (int j = 0; j < m; ++j) v *= load_in<BF16>(x, static_cast<size_t>(r) * D + ((pf.idx >> (8 * j)) & 255));
+    phi[e] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+#define TL_DECODE_CFGS(X) \
+  X(16, 16, 1)            \
+  X(16, 64, 1)            \
+  X(16, 16, 3)            \
+  X(16, 64, 3)            \
+  X(16, 16, 5)            \
+  X(16, 64, 5)            \
+  X(64, 16, 1)            \
+  X(64, 64, 1)            \
+  X(64, 16, 3)            \
+  X(64, 64, 3)
+
+hipError_t decode_launch(int d, int dv, int n_terms, bool bf16, const DecodeArgs& a,
+                         hipStream_t stream) {
+#define X(D, DV, NT)                                                                        \
+  if (d == D && dv == DV && n_terms == NT) {                                                \
+    if (bf16)                                                                               \
+      hipLaunchKernelGGL((decode_kernel<D, DV, NT, true>), dim3(a.BH), dim3(256), 0, stream, a);  \
+    else                                                                                    \
+      hipLaunchKernelGGL((decode_kernel<D, DV, NT, false>), dim3(a.BH), dim3(256), 0, stream, a); \
+    return hipGetLastError();                                                               \
+  }
+  TL_DECODE_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t feature_map_launch(int d, int n_terms, bool bf16, const void* x, int64_t rows,
+                              float* phi, const OrderScale& sc, hipStream_t stream) {
+  const int64_t total = rows * feature_count(d, n_terms);
+  const int64_t want = (total + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+#define X(D, NT)                                                                                  \
+  if (d == D && n_terms == NT) {                                                                  \
+    if (bf16)                                                                                     \
+      hipLaunchKernelGGL((feature_map_kernel<D, NT, true>), dim3(blocks), dim3(256), 0, stream, x, \
+                         rows, phi, sc);                                                          \
+    else                                                                                          \
+      hipLaunchKernelGGL((feature_map_kernel<D, NT, false>), dim3(blocks), dim3(256), 0, stream,  \
+                         x, rows, phi, sc);                                                       \
+    return hipGetLastError();                                                                     \
+  }
+  X(16, 1) X(16, 3) X(16, 5) X(64, 1) X(64, 3)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tl

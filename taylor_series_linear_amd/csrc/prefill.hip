@@ -1,0 +1,713 @@
+// Chunked causal prefill of Taylor-series linear attention on gfx950.
+//
+// Method ("Expanding Attention: A Taylor-Series Route to Linear-Time
+// Transformers with a Fixed Number of Recurrent States"):
+//   o_t = sum_{s<=t} w(q_t.k_s/a) v_s / sum_{s<=t} w(q_t.k_s/a),
+//   w(x) = sum_{m<n} x^m/m!.
+// "Time" on that page splits prefill into a state part and diagonal blocks
+// of size c: for a chunk of c tokens,
+//   O  = phi~(Q_c) S_<c   (read-out of the state of all earlier tokens)
+//      + P V_c            (P_ij = w(q_i.k_j/a), j <= i inside the chunk)
+//   S += phi(K_c)^T [V_c, 1]   (per-order states, "Memory")
+// with phi~ = phi with alpha_m = 1/(m! a^m) folded in. The trailing column
+// of ones carries the denominator through the same contractions. States are
+// additive (closing paragraph of the page), which gives the sequence split
+// below.
+//
+// Work decomposition on the chip:
+//  * A workgroup owns one (head, segment, feature slice). Segment sums of
+//    earlier segments arrive from a first pass (MODE_SEGSUM); the state slice
+//    [FS x (dv+16)] lives in the accumulator registers of NW = dv/16 + 1
+//    waves, wave w holding dv columns 16w..16w+15 (the last wave holds the
+//    ones column, i.e. the denominator state z).
+//  * Per chunk: stage Q, K and V^T (+ ones row) in LDS; generate phi~(Q)
+//    [C x FS] and phi(K) [FS x C] in LDS; score tiles K Q^T on MFMA with the
+//    polynomial and causal mask applied in registers; read-out, intra-chunk
+//    and update contractions on MFMA.
+//  * With one slice (small feature widths) the workgroup normalises and
+//    writes o itself; with several slices each writes a partial
+//    (numerator, denominator) and a small kernel sums and divides.
+#include "features.hpp"
+#include "internal.hpp"
+#include "mma.hpp"
+
+#include <utility>
+
+namespace tl {
+
+// ---------------------------------------------------------------------------
+// compile-time helpers
+// ---------------------------------------------------------------------------
+
+template <int B, class Fn, int... Is>
+__device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
+  (fn(std::integral_constant<int, B + Is>{}), ...);
+}
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (E > B) static_for_impl<B>(fn, std::make_integer_sequence<int, E - B>{});
+}
+
+// 1/m! as float, m < n (Horner coefficients of the truncated exponential).
+template <int NT>
+__device__ __forceinline__ float taylor_poly(float t) {
+  // w(t) = sum_{m<NT} t^m/m!, Horner from the highest term down.
+  float p = static_cast<float>(1.0 / static_cast<double>(factorial(NT - 1)));
+  static_for<0, NT - 1>([&](auto jj) {
+    constexpr int m = NT - 2 - decltype(jj)::value;
+    p = __builtin_fmaf(p, t, static_cast<float>(1.0 / static_cast<double>(factorial(m))));
+  });
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// configuration of one instantiation
+// ---------------------------------------------------------------------------
+
+template <int D_, int DV_, int NT_, bool BF16_, int FS_, int C_, bool UNROLL_>
+struct PCfg {
+  static constexpr int D = D_, DV = DV_, NT = NT_, FS = FS_, C = C_;
+  static constexpr bool BF16 = BF16_, UNROLL = UNROLL_;
+  using M = Mma<BF16>;
+  using E = typename M::elem;
+  static constexpr int ES = sizeof(E);
+  static constexpr int F = feature_count(D, NT);
+  static constexpr int G = (F + FS - 1) / FS;
+  static constexpr int NW = DV / 16 + 1;
+  static constexpr int NTHR = NW * 64;
+  static constexpr int DVP = NW * 16;
+  static constexpr int FT = FS / 16;   // 16-feature tiles per slice
+  static constexpr int KSF = FS / 32;  // read-out k-steps
+  static constexpr int QT = C / 16;    // query tiles per chunk
+  static constexpr int KSC = C / 32;   // key k-steps per chunk
+  static constexpr int PADE = 16 / ES; // 16 bytes of padding, in elements
+  static constexpr int XP = D + PADE;  // Q/K tile pitch
+  static constexpr int PQ = FS + PADE; // phi~(Q) pitch (query-major)
+  static constexpr int PK = C + PADE;  // phi(K)^T, V^T pitch (key-contiguous)
+  static constexpr int PP = C + PADE;  // P^T pitch (query-major, keys contiguous)
+  static constexpr int PPITCH = DV + 4;  // partial-output row pitch (floats)
+  // LDS layout (bytes)
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_K = OFF_Q + C * XP * ES;
+  static constexpr int OFF_V = OFF_K + C * XP * ES;
+  static constexpr int OFF_PQ = OFF_V + DVP * PK * ES;
+  static constexpr int OFF_PK = OFF_PQ + C * PQ * ES;
+  static constexpr int OFF_P = OFF_PK + FS * PK * ES;
+  static constexpr int OFF_DEN = OFF_P + C * PP * ES;
+  static constexpr int LDS = OFF_DEN + C * 4;
+  static_assert(FS % 32 == 0 && C % 32 == 0 && DV % 16 == 0, "tile multiples");
+  static_assert(D % 16 == 0, "head dim multiple of 16");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  // score tiles (kt, qt) needed per chunk: key tiles up to the end of the
+  // 32-key step that contains the diagonal tile
+  static constexpr int NTILES = [] {
+    int n = 0;
+    for (int qt = 0; qt < C / 16; ++qt) n += 2 * (qt / 2) + 2;
+    return n;
+  }();
+};
+
+template <class Cfg>
+struct TileList {
+  int kt[Cfg::NTILES];
+  int qt[Cfg::NTILES];
+};
+template <class Cfg>
+constexpr TileList<Cfg> make_tiles() {
+  TileList<Cfg> t{};
+  int n = 0;
+  for (int qt = 0; qt < Cfg::QT; ++qt)
+    for (int kt = 0; kt < 2 * (qt / 2) + 2; ++kt) {
+      t.kt[n] = kt;
+      t.qt[n] = qt;
+      ++n;
+    }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// feature generation, unrolled (whole basis in one slice; small widths)
+// ---------------------------------------------------------------------------
+
+// Value of feature f for a row x (query side: x already divided by a and the
+// 1/m! folded into the constants).
+template <int D, int NT, bool QSIDE, int f>
+__device__ __forceinline__ float feat_val(const float (&x)[D]) {
+  if constexpr (f >= feature_count(D, NT)) {
+    return 0.f;
+  } else {
+    constexpr GenConst gc = gen_const<D, NT, QSIDE>(f);
+    if constexpr (gc.m == 0) {
+      return static_cast<float>(gc.G);
+    } else {
+      float p = static_cast<float>(gc.G);
+      static_for<0, gc.m - 1>([&](auto jj) { p = p * x[gc.idx[decltype(jj)::value]]; });
+      float v = p * x[gc.idx[gc.m - 1]];
+      if constexpr (gc.R != 1.0) v = v * static_cast<float>(gc.R);
+      return v;
+    }
+  }
+}
+
+// phi~(q) for features [8*PB, 8*PE) of one token, written as 8-wide packs
+// into its row of the query-major tile.
+template <class Cfg, int PB, int PE>
+__device__ __forceinline__ void gen_q_packs(const float (&x)[Cfg::D], typename Cfg::E* row) {
+  using E = typename Cfg::E;
+  static_for<PB, PE>([&](auto pi) {
+    constexpr int p = decltype(pi)::value;
+    E vals[8];
+    static_for<0, 8>([&](auto ji) {
+      constexpr int f = 8 * p + decltype(ji)::value;
+      vals[decltype(ji)::value] = Cfg::M::cvt(feat_val<Cfg::D, Cfg::NT, true, f>(x));
+    });
+    if constexpr (Cfg::BF16) {
+      bf16x8 pk;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pk[j] = vals[j];
+      *reinterpret_cast<bf16x8*>(row + 8 * p) = pk;
+    } else {
+      f32x4 a = {vals[0], vals[1], vals[2], vals[3]};
+      f32x4 b = {vals[4], vals[5], vals[6], vals[7]};
+      *reinterpret_cast<f32x4*>(row + 8 * p) = a;
+      *reinterpret_cast<f32x4*>(row + 8 * p + 4) = b;
+    }
+  });
+}
+
+// phi(k) for features [8*PB, 8*PE) of one token, into its column of the
+// feature-major tile.
+template <class Cfg, int PB, int PE>
+__device__ __forceinline__ void gen_k_packs(const float (&x)[Cfg::D], typename Cfg::E* col) {
+  static_for<8 * PB, 8 * PE>([&](auto fi) {
+    constexpr int f = decltype(fi)::value;
+    col[f * Cfg::PK] = Cfg::M::cvt(feat_val<Cfg::D, Cfg::NT, false, f>(x));
+  });
+}
+
+template <class Cfg, bool QSIDE>
+__device__ __forceinline__ void gen_unrolled(int w, const float (&x)[Cfg::D], typename Cfg::E* dst) {
+  constexpr int NP = Cfg::FS / 8;
+  static_for<0, Cfg::NW>([&](auto wi) {
+    constexpr int W = decltype(wi)::value;
+    constexpr int PB = W * NP / Cfg::NW;
+    constexpr int PE = (W + 1) * NP / Cfg::NW;
+    if (w == W) {
+      if constexpr (QSIDE)
+        gen_q_packs<Cfg, PB, PE>(x, dst);
+      else
+        gen_k_packs<Cfg, PB, PE>(x, dst);
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// feature generation, table-driven (large widths; one slice of the basis)
+// ---------------------------------------------------------------------------
+
+template <int D, int NT>
+__device__ const PackedTable<D, NT> g_ptab = make_packed<D, NT>();
+
+// Lanes own features, loop over the chunk's tokens; x rows are read from LDS
+// (all lanes read the same row: broadcast).
+template <class Cfg, bool QSIDE>
+__device__ __forceinline__ void gen_table(int w, int lane, int f0, const typename Cfg::E* X,
+                                          typename Cfg::E* dst, float inv_a) {
+  using E = typename Cfg::E;
+  constexpr int NB = (Cfg::FS + 63) / 64;
+  const auto& tab = g_ptab<Cfg::D, Cfg::NT>;
+  for (int blk = w; blk < NB; blk += Cfg::NW) {
+    const int fl = 64 * blk + lane;
+    if (fl >= Cfg::FS) continue;
+    const int f = f0 + fl;
+    float cf = 0.f;
+    uint32_t idx = 0;
+    int m = 0;
+    if (f < Cfg::F) {
+      const PackedFeature e = tab.e[f];
+      idx = e.idx;
+      m = static_cast<int>(e.m);
+      cf = e.w;
+      if (QSIDE) {
+        cf *= e.inv_mfact;
+        for (int j = 0; j < m; ++j) cf *= inv_a;
+      }
+    }
+    const int i0 = idx & 255, i1 = (idx >> 8) & 255, i2 = (idx >> 16) & 255, i3 = idx >> 24;
+    if constexpr (QSIDE) {
+      for (int t = 0; t < Cfg::C; ++t) {
+        const E* xr = X + t * Cfg::XP;
+        float v = cf;
+        if (m > 0) v *= static_cast<float>(xr[i0]);
+        if (m > 1) v *= static_cast<float>(xr[i1]);
+        if (m > 2) v *= static_cast<float>(xr[i2]);
+        if (m > 3) v *= static_cast<float>(xr[i3]);
+        dst[t * Cfg::PQ + fl] = Cfg::M::cvt(v);
+      }
+    } else {
+      for (int t0 = 0; t0 < Cfg::C; t0 += 8) {
+        E vals[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const E* xr = X + (t0 + j) * Cfg::XP;
+          float v = cf;
+          if (m > 0) v *= static_cast<float>(xr[i0]);
+          if (m > 1) v *= static_cast<float>(xr[i1]);
+          if (m > 2) v *= static_cast<float>(xr[i2]);
+          if (m > 3) v *= static_cast<float>(xr[i3]);
+          vals[j] = Cfg::M::cvt(v);
+        }
+        E* out = dst + fl * Cfg::PK + t0;
+        if constexpr (Cfg::BF16) {
+          bf16x8 pk;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pk[j] = vals[j];
+          *reinterpret_cast<bf16x8*>(out) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(out) = f32x4{vals[0], vals[1], vals[2], vals[3]};
+          *reinterpret_cast<f32x4*>(out + 4) = f32x4{vals[4], vals[5], vals[6], vals[7]};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+
+enum { MODE_SEGSUM = 0, MODE_MAIN = 1 };
+
+template <class Cfg, int MODE>
+__global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
+  using M = typename Cfg::M;
+  using E = typename Cfg::E;
+  using frag = typename M::frag;
+  constexpr int D = Cfg::D, DV = Cfg::DV, C = Cfg::C, NW = Cfg::NW, G = Cfg::G;
+  constexpr int FT = Cfg::FT, QT = Cfg::QT, KSC = Cfg::KSC, KSF = Cfg::KSF;
+  constexpr bool MAIN = MODE == MODE_MAIN;
+
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
+  E* sQ = reinterpret_cast<E*>(smem + Cfg::OFF_Q);
+  E* sK = reinterpret_cast<E*>(smem + Cfg::OFF_K);
+  E* sV = reinterpret_cast<E*>(smem + Cfg::OFF_V);
+  E* sPQ = reinterpret_cast<E*>(smem + Cfg::OFF_PQ);
+  E* sPK = reinterpret_cast<E*>(smem + Cfg::OFF_PK);
+  E* sP = reinterpret_cast<E*>(smem + Cfg::OFF_P);
+  float* sDen = reinterpret_cast<float*>(smem + Cfg::OFF_DEN);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int g4 = lane >> 4;
+  const int c = lane & 15;
+
+  // block -> (unit, slice); the G slices of a unit share an XCD (b % 8).
+  const int PL = MAIN ? a.P : a.P - 1;  // segments handled by this launch
+  const int nunits = a.BH * PL;
+  const int b = blockIdx.x;
+  const int gsl = (b >> 3) % G;
+  const int unit = (b & 7) + 8 * ((b >> 3) / G);
+  if (unit >= nunits) return;
+  const int bh = unit / PL;
+  const int p = unit - bh * PL;
+  const int f0 = gsl * Cfg::FS;
+  const int N = a.N;
+  const bool want_out = MAIN && a.o != nullptr;
+  const bool want_state = MAIN && a.S != nullptr && p == a.P - 1;
+  if (MAIN && !want_out && !want_state) return;
+
+  const int t0 = p * a.L;
+  const int t1 = min(N, t0 + a.L);
+
+  const E* qh = reinterpret_cast<const E*>(a.q) + static_cast<size_t>(bh) * N * D;
+  const E* kh = reinterpret_cast<const E*>(a.k) + static_cast<size_t>(bh) * N * D;
+  const E* vh = reinterpret_cast<const E*>(a.v) + static_cast<size_t>(bh) * N * DV;
+
+  // constant part of V^T: padding rows below the ones row
+  for (int i = tid; i < (Cfg::DVP - DV - 1) * Cfg::PK; i += Cfg::NTHR)
+    sV[(DV + 1) * Cfg::PK + i] = M::cvt(0.f);
+
+  // ---- initial state of this slice ------------------------------------------
+  f32x4 S[FT];
+#pragma unroll
+  for (int ft = 0; ft < FT; ++ft) S[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (MAIN) {
+    if (a.S0 != nullptr) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = f0 + 16 * ft + 4 * g4 + i;
+          float val = 0.f;
+          if (f < Cfg::F) {
+            if (w < NW - 1)
+              val = a.S0[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c];
+            else if (c == 0)
+              val = a.z0[static_cast<size_t>(bh) * Cfg::F + f];
+          }
+          S[ft][i] = val;
+        }
+    }
+    const int PS = a.P - 1;
+    for (int pp = 0; pp < p; ++pp) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.seg) +
+                         ((((static_cast<size_t>(bh) * PS + pp) * G + gsl) * NW + w) * FT) * 64 + lane;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) S[ft] += src[ft * 64];
+    }
+  }
+
+  const float inv_a = a.inv_a;
+
+  // ---- chunk loop ------------------------------------------------------------
+  for (int c0 = t0; c0 < t1; c0 += C) {
+    const int nv = min(C, t1 - c0);
+    const bool last_chunk = c0 + C >= t1;
+    const bool do_update = !MAIN || !last_chunk || want_state;
+
+    // stage Q, K (row-major) and V^T (+ ones row) in LDS
+    {
+      constexpr int EV = 16 / Cfg::ES;   // elements per 16-byte vector
+      constexpr int VPR = D / EV;        // vectors per q/k row
+      for (int i = tid; i < C * VPR; i += Cfg::NTHR) {
+        const int row = i / VPR, col = (i % VPR) * EV;
+        uint4 vk = {0, 0, 0, 0}, vq = {0, 0, 0, 0};
+        if (row < nv) {
+          vk = *reinterpret_cast<const uint4*>(kh + static_cast<size_t>(c0 + row) * D + col);
+          if (want_out) vq = *reinterpret_cast<const uint4*>(qh + static_cast<size_t>(c0 + row) * D + col);
+        }
+        *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = vk;
+        if (want_out) *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = vq;
+      }
+      constexpr int VPRV = DV / EV;
+      for (int i = tid; i < C * VPRV; i += Cfg::NTHR) {
+        const int row = i / VPRV, col = (i % VPRV) * EV;
+        uint4 vv = {0, 0, 0, 0};
+        if (row < nv) vv = *reinterpret_cast<const uint4*>(vh + static_cast<size_t>(c0 + row) * DV + col);
+        const E* e = reinterpret_cast<const E*>(&vv);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) sV[(col + j) * Cfg::PK + row] = e[j];
+      }
+      for (int i = tid; i < C; i += Cfg::NTHR) sV[DV * Cfg::PK + i] = M::cvt(i < nv ? 1.f : 0.f);
+    }
+    __syncthreads();
+
+    // features and score tiles
+    if constexpr (Cfg::UNROLL) {
+      if (lane < C) {
+        float x[D];
+        if (want_out) {
+#pragma unroll
+          for (int j = 0; j < D; ++j) x[j] = static_cast<float>(sQ[lane * Cfg::XP + j]) * inv_a;
+          gen_unrolled<Cfg, true>(w, x, sPQ + lane * Cfg::PQ);
+        }
+        if (do_update) {
+#pragma unroll
+          for (int j = 0; j < D; ++j) x[j] = static_cast<float>(sK[lane * Cfg::XP + j]);
+          gen_unrolled<Cfg, false>(w, x, sPK + lane);
+        }
+      }
+    } else {
+      if (want_out) gen_table<Cfg, true>(w, lane, f0, sQ, sPQ, inv_a);
+      if (do_update) gen_table<Cfg, false>(w, lane, f0, sK, sPK, inv_a);
+    }
+    if (want_out && gsl == 0) {
+      constexpr TileList<Cfg> tiles = make_tiles<Cfg>();
+      static_for<0, Cfg::NTILES>([&](auto tii) {
+        constexpr int ti = decltype(tii)::value;
+        constexpr int kt = tiles.kt[ti], qt = tiles.qt[ti];
+        if (ti % NW == w) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (kt <= qt) {
+            if constexpr (D == 16) {
+              const auto ak = *reinterpret_cast<const typename M::half*>(sK + (16 * kt + c) * Cfg::XP + 4 * g4);
+              const auto bq = *reinterpret_cast<const typename M::half*>(sQ + (16 * qt + c) * Cfg::XP + 4 * g4);
+              acc = M::hstep(ak, bq, acc);
+            } else {
+#pragma unroll
+              for (int u = 0; u < D / 32; ++u) {
+                const frag ak = lds_frag8(sK + (16 * kt + c) * Cfg::XP + 32 * u + 8 * g4);
+                const frag bq = lds_frag8(sQ + (16 * qt + c) * Cfg::XP + 32 * u + 8 * g4);
+                acc = M::step(ak, bq, acc);
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float wv = taylor_poly<Cfg::NT>(acc[i] * inv_a);
+              if (kt == qt && 4 * g4 + i > c) wv = 0.f;  // causal mask (key > query)
+              acc[i] = wv;
+            }
+          }
+          E* dst = sP + (16 * qt + c) * Cfg::PP + 16 * kt + 4 * g4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = M::cvt(acc[i]);
+        }
+      });
+    }
+    __syncthreads();
+
+    if (want_out) {
+      // read-out of the state: O^T[dv tile w] = S^T phi~(Q)^T
+      f32x4 acc[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KSF; ++t) {
+        frag sa;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sa[j] = M::cvt(S[2 * t][j]);
+          sa[j + 4] = M::cvt(S[2 * t + 1][j]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const frag bq = lds_frag_split(sPQ + (16 * qt + c) * Cfg::PQ + 32 * t + 4 * g4);
+          acc[qt] = M::step(sa, bq, acc[qt]);
+        }
+      }
+      // intra-chunk term: O^T += [V,1]^T P^T (first slice only)
+      if (gsl == 0) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int u = 0; u <= qt / 2; ++u) {
+            const frag av = lds_frag8(sV + (16 * w + c) * Cfg::PK + 32 * u + 8 * g4);
+            const frag bp = lds_frag8(sP + (16 * qt + c) * Cfg::PP + 32 * u + 8 * g4);
+            acc[qt] = M::step(av, bp, acc[qt]);
+          }
+      }
+      if constexpr (G == 1) {
+        // denominator: row DV of O^T = wave NW-1, lane group 0, element 0
+        if (w == NW - 1 && g4 == 0) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) sDen[16 * qt + c] = acc[qt][0];
+        }
+        __syncthreads();
+        if (w < NW - 1) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const int qi = 16 * qt + c;
+            if (qi < nv) {
+              const float r = 1.f / sDen[qi];
+              const size_t off = (static_cast<size_t>(bh) * N + c0 + qi) * DV + 16 * w + 4 * g4;
+              if (a.out_bf16) {
+                bf16x4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(acc[qt][i] * r);
+                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
+              } else {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = acc[qt] * r;
+              }
+            }
+          }
+        }
+      } else {
+        float* pp = a.part + ((static_cast<size_t>(gsl) * a.BH + bh) * N + c0) * Cfg::PPITCH;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const int qi = 16 * qt + c;
+          if (qi < nv) {
+            if (w < NW - 1)
+              *reinterpret_cast<f32x4*>(pp + qi * Cfg::PPITCH + 16 * w + 4 * g4) = acc[qt];
+            else if (g4 == 0)
+              pp[qi * Cfg::PPITCH + DV] = acc[qt][0];
+          }
+        }
+      }
+    }
+
+    if (do_update) {
+      // S[:, dv tile w] += phi(K)^T [V,1][:, dv tile w]
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int u = 0; u < KSC; ++u) {
+          const frag ak = lds_frag8(sPK + (16 * ft + c) * Cfg::PK + 32 * u + 8 * g4);
+          const frag bv = lds_frag8(sV + (16 * w + c) * Cfg::PK + 32 * u + 8 * g4);
+          S[ft] = M::step(ak, bv, S[ft]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // ---- results ---------------------------------------------------------------
+  if constexpr (MAIN) {
+    if (want_state && a.defer_state) {
+      f32x4* dst = reinterpret_cast<f32x4*>(a.fin) +
+                   (((static_cast<size_t>(bh) * G + gsl) * NW + w) * FT) * 64 + lane;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) dst[ft * 64] = S[ft];
+    } else if (want_state) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int f = f0 + 16 * ft + 4 * g4 + i;
+          if (f < Cfg::F) {
+            if (w < NW - 1)
+              a.S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = S[ft][i];
+            else if (c == 0)
+              a.z[static_cast<size_t>(bh) * Cfg::F + f] = S[ft][i];
+          }
+        }
+    }
+  } else {
+    const int PS = a.P - 1;
+    f32x4* dst = reinterpret_cast<f32x4*>(a.seg) +
+                 ((((static_cast<size_t>(bh) * PS + p) * G + gsl) * NW + w) * FT) * 64 + lane;
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) dst[ft * 64] = S[ft];
+  }
+}
+
+// Sum the per-slice partial (numerator, denominator) rows and divide.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int G,
+                                                      int64_t rows, int dv, int pitch, void* o,
+                                                      int out_bf16) {
+  const int nq = dv / 4;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= rows * nq) return;
+  const int64_t r = e / nq;
+  const int dq = static_cast<int>(e - r * nq);
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int g = 0; g < G; ++g) {
+    const float* src = part + (static_cast<int64_t>(g) * rows + r) * pitch;
+    num += *reinterpret_cast<const f32x4*>(src + 4 * dq);
+    den += src[dv];
+  }
+  const float rcp = 1.f / den;
+  const int64_t off = r * dv + 4 * dq;
+  if (out_bf16) {
+    bf16x4 ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(num[i] * rcp);
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(o) + off) = ov;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + off) = num * rcp;
+  }
+}
+
+// S = S0 (or zero), z = z0 (or zero): the state after zero tokens.
+__global__ __launch_bounds__(256) void state_init_kernel(const float* S0, const float* z0, float* S,
+                                                         float* z, int64_t nS, int64_t nz) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < nS) S[i] = S0 ? S0[i] : 0.f;
+  if (i < nz) z[i] = z0 ? z0[i] : 0.f;
+}
+
+// Scatter the staged final state (accumulator layout) into S [F, dv] and z [F].
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NTHR) void state_store_kernel(const float* fin, float* S, float* z,
+                                                                int BH) {
+  constexpr int NW = Cfg::NW, FT = Cfg::FT, G = Cfg::G, DV = Cfg::DV;
+  const int bh = blockIdx.x / G, gsl = blockIdx.x % G;
+  if (bh >= BH) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, c = lane & 15;
+  const f32x4* src = reinterpret_cast<const f32x4*>(fin) +
+                     (((static_cast<size_t>(bh) * G + gsl) * NW + w) * FT) * 64 + lane;
+  for (int ft = 0; ft < FT; ++ft) {
+    const f32x4 val = src[ft * 64];
+    for (int i = 0; i < 4; ++i) {
+      const int f = gsl * Cfg::FS + 16 * ft + 4 * g4 + i;
+      if (f < Cfg::F) {
+        if (w < NW - 1)
+          S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = val[i];
+        else if (c == 0)
+          z[static_cast<size_t>(bh) * Cfg::F + f] = val[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+template <class Cfg>
+static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int G = Cfg::G;
+  auto blocks_for = [](int units) { return 8 * G * ((units + 7) / 8); };
+  if (a.P > 1) {
+    const int units = a.BH * (a.P - 1);
+    hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_SEGSUM>), dim3(blocks_for(units)), dim3(Cfg::NTHR), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_MAIN>), dim3(blocks_for(a.BH * a.P)), dim3(Cfg::NTHR), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.defer_state) {
+    hipLaunchKernelGGL((state_store_kernel<Cfg>), dim3(a.BH * G), dim3(Cfg::NTHR), 0, stream, a.fin, a.S,
+                       a.z, a.BH);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (G > 1 && a.o != nullptr) {
+    const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
+    const int64_t n = rows * (Cfg::DV / 4);
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                       a.part, G, rows, Cfg::DV, Cfg::PPITCH, a.o, a.out_bf16);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// Instantiation table: (d, dv, n_terms, bf16) -> slice width, chunk, generator.
+#define TL_PREFILL_CFGS(X)                  \
+  X(16, 16, 1, true, 32, 64, true)          \
+  X(16, 16, 1, false, 32, 64, true)         \
+  X(16, 64, 1, true, 32, 64, true)          \
+  X(16, 64, 1, false, 32, 64, true)         \
+  X(16, 16, 3, true, 160, 64, true)         \
+  X(16, 16, 3, false, 160, 64, true)        \
+  X(16, 64, 3, true, 160, 64, true)         \
+  X(16, 64, 3, false, 160, 64, true)        \
+  X(16, 16, 5, true, 608, 32, false)        \
+  X(16, 16, 5, false, 256, 32, false)       \
+  X(16, 64, 5, true, 608, 32, false)        \
+  X(16, 64, 5, false, 256, 32, false)       \
+  X(64, 16, 1, true, 32, 64, true)          \
+  X(64, 16, 1, false, 32, 64, true)         \
+  X(64, 64, 1, true, 32, 64, true)          \
+  X(64, 64, 1, false, 32, 64, true)         \
+  X(64, 16, 3, true, 544, 32, false)        \
+  X(64, 16, 3, false, 128, 32, false)       \
+  X(64, 64, 3, true, 544, 32, false)        \
+  X(64, 64, 3, false, 128, 32, false)
+
+bool prefill_traits(int d, int dv, int n_terms, bool bf16, PrefillTraits* t) {
+#define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
+  if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_) {             \
+    using Cf = PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>;                      \
+    *t = PrefillTraits{Cf::F, Cf::FS, Cf::G, Cf::C, Cf::NW};               \
+    return true;                                                           \
+  }
+  TL_PREFILL_CFGS(X)
+#undef X
+  return false;
+}
+
+hipError_t prefill_launch(int d, int dv, int n_terms, bool bf16, const PrefillArgs& a,
+                          hipStream_t stream) {
+#define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
+  if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_)               \
+    return launch_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(a, stream);
+  TL_PREFILL_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t state_init_launch(const float* S0, const float* z0, float* S, float* z, int64_t BH,
+                             int F, int dv, hipStream_t stream) {
+  const int64_t nS = BH * F * dv, nz = BH * F;
+  if (nS == 0) return hipSuccess;
+  hipLaunchKernelGGL(state_init_kernel, dim3(static_cast<unsigned>((nS + 255) / 256)), dim3(256), 0, stream,
+                     S0, z0, S, z, nS, nz);
+  return hipGetLastError();
+}
+
+}  // namespace tl

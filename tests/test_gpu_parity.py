@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (normwise relative error per head, max over heads): 1e-4 for fp32
+inputs, 2e-2 for bf16 inputs with fp32 accumulation.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import taylor_oracle as T
+import workloads as W
+from tests.helpers import normwise_rel, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines too
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import taylor_series_linear_amd as tl  # noqa: E402
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+CONFIGS = [(16, 16, 1), (16, 64, 1), (16, 16, 3), (16, 64, 3), (16, 16, 5), (16, 64, 5),
+           (64, 16, 1), (64, 64, 1), (64, 16, 3), (64, 64, 3)]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _inputs(B, H, N, d, dv, dtype, seed, qk="normal"):
+    return W.make_qkv(B, H, N, d, dv, dtype, seed, qk)
+
+
+def _run_prefill(x, n, a, dtype, **kw):
+    q = to_device(x["q"], dtype)
+    k = to_device(x["k"], dtype)
+    v = to_device(x["v"], dtype)
+    r = tl.prefill(q, k, v, n, a, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _qk_kind(d, n):
+    # order-4 keeps |q.k/a| <= 1 as the workloads do (rows at norm 2, a = 4)
+    return "l2x2" if n == 5 else "normal"
+
+
+@pytest.mark.parametrize("d,n", [(16, 1), (16, 3), (16, 5), (64, 1), (64, 3)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fold", [False, True])
+def test_feature_map(d, n, dtype, fold):
+    rows = 37
+    x = W.make_qkv(1, 1, rows, d, 16, dtype, 11)
+    say("feature_map", d, n, dtype, fold)
+    phi = tl.feature_map(to_device(x["q"][0, 0], dtype), n, a=(math.sqrt(d) if fold else None))
+    torch.cuda.synchronize()
+    ref = T.phi(x["q64"][0, 0], n, a=(math.sqrt(d) if fold else None))
+    err = np.max(np.abs(to_f64(phi) - ref)) / np.max(np.abs(ref))
+    assert err < 2e-6, err
+    # Gram identity on the device output: phi(x).phi(y) = w_n(x.y/a) (folded)
+    if fold:
+        g = to_f64(phi) @ to_f64(phi).T
+        t = x["q64"][0, 0] @ x["q64"][0, 0].T / math.sqrt(d)
+        assert np.max(np.abs(g - T.taylor_weight(t, n))) < 1e-4 * np.max(np.abs(g))
+
+
+@pytest.mark.parametrize("d,dv,n", CONFIGS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 37, 64, 200, 1000])
+def test_prefill_small(d, dv, n, dtype, N):
+    B, H = 1, 2
+    a = math.sqrt(d)
+    x = _inputs(B, H, N, d, dv, dtype, 100 + N, _qk_kind(d, n))
+    say("prefill", d, dv, n, dtype, N)
+    o, S, z = _run_prefill(x, n, a, dtype, out_dtype=torch.float32, return_state=True)
+    ref = T.direct(x["q64"], x["k64"], x["v64"], n, a)
+    err = normwise_rel(to_f64(o), ref)
+    say("  err", err)
+    assert err < TOL[dtype], err
+    Sr, zr = T.state(x["k64"], x["v64"], n)
+    assert normwise_rel(to_f64(S), Sr) < TOL[dtype]
+    assert normwise_rel(to_f64(z)[..., None], zr[..., None]) < TOL[dtype]
+
+
+@pytest.mark.parametrize("d,dv,n", [(16, 64, 3), (16, 16, 1), (64, 64, 3), (16, 64, 5)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_multi_segment(d, dv, n, dtype):
+    # long enough that the sequence is split into several segments
+    B, H, N = 1, 1, 3000
+    a = math.sqrt(d)
+    x = _inputs(B, H, N, d, dv, dtype, 7, _qk_kind(d, n))
+    say("prefill multi-segment", d, dv, n, dtype)
+    o, S, z = _run_prefill(x, n, a, dtype, out_dtype=torch.float32, return_state=True)
+    rows = np.unique(np.r_[0:70, 500:530, 1000:1100, 2900:3000])
+    ref = T.direct(x["q64"], x["k64"], x["v64"], n, a, rows=rows)
+    err = normwise_rel(to_f64(o)[:, :, rows], ref)
+    say("  err", err)
+    assert err < TOL[dtype]
+    Sr, zr = T.state(x["k64"], x["v64"], n)
+    assert normwise_rel(to_f64(S), Sr) < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("N1,N2", [(100, 37), (1500, 2100)])
+def test_continuation(dtype, inplace, N1, N2):
+    d, dv, n, a = 16, 64, 3, 4.0
+    x = _inputs(1, 2, N1 + N2, d, dv, dtype, 21)
+    q, k, v = (to_device(x[s], dtype) for s in "qkv")
+    say("continuation", dtype, inplace, N1, N2)
+    o1, S1, z1 = tl.prefill(q[:, :, :N1].contiguous(), k[:, :, :N1].contiguous(), v[:, :, :N1].contiguous(),
+                            n, a, out_dtype=torch.float32, return_state=True)
+    if inplace:
+        o2, S2, z2 = tl.prefill(q[:, :, N1:].contiguous(), k[:, :, N1:].contiguous(), v[:, :, N1:].contiguous(),
+                                n, a, S1, z1, out_dtype=torch.float32, S=S1, z=z1)
+        assert S2.data_ptr() == S1.data_ptr()
+    else:
+        o2, S2, z2 = tl.prefill(q[:, :, N1:].contiguous(), k[:, :, N1:].contiguous(), v[:, :, N1:].contiguous(),
+                                n, a, S1, z1, out_dtype=torch.float32, return_state=True)
+    torch.cuda.synchronize()
+    full = T.direct(x["q64"], x["k64"], x["v64"], n, a)
+    assert normwise_rel(to_f64(o1), full[:, :, :N1]) < TOL[dtype]
+    assert normwise_rel(to_f64(o2), full[:, :, N1:]) < TOL[dtype]
+    Sr, zr = T.state(x["k64"], x["v64"], n)
+    assert normwise_rel(to_f64(S2), Sr) < TOL[dtype]
+    assert normwise_rel(to_f64(z2)[..., None], zr[..., None]) < TOL[dtype]
+
+
+def test_empty_inputs():
+    d, dv, n = 16, 64, 3
+    F = T.n_features(d, n)
+    say("empty inputs")
+    e = torch.empty((1, 2, 0, d), device="cuda:0")
+    ev = torch.empty((1, 2, 0, dv), device="cuda:0")
+    S0 = torch.randn((1, 2, F, dv), device="cuda:0")
+    z0 = torch.rand((1, 2, F), device="cuda:0")
+    o, S, z = tl.prefill(e, e, ev, n, 4.0, S0, z0, return_state=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 2, 0, dv)
+    assert torch.equal(S, S0) and torch.equal(z, z0)
+    o, S, z = tl.prefill(e, e, ev, n, 4.0, return_state=True)
+    torch.cuda.synchronize()
+    assert float(S.abs().max()) == 0.0 and float(z.abs().max()) == 0.0
+    eb = torch.empty((0, 2, 10, d), device="cuda:0")
+    o = tl.prefill(eb, eb, torch.empty((0, 2, 10, dv), device="cuda:0"), n, 4.0)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 10, dv)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_special_cases(dtype):
+    d, dv, N = 16, 64, 300
+    x = _inputs(1, 1, N, d, dv, dtype, 33)
+    say("special cases", dtype)
+    prefix_mean = np.cumsum(x["v64"][0, 0], axis=0) / np.arange(1, N + 1)[:, None]
+    # n = 1: prefix mean of v
+    o = _run_prefill(x, 1, 4.0, dtype, out_dtype=torch.float32)
+    assert normwise_rel(to_f64(o)[0, 0][None], prefix_mean[None], 1) < TOL[dtype]
+    # q = 0: prefix mean for any n
+    x0 = dict(x)
+    x0["q"] = np.zeros_like(x["q"])
+    o = _run_prefill(x0, 3, 4.0, dtype, out_dtype=torch.float32)
+    assert normwise_rel(to_f64(o)[0, 0][None], prefix_mean[None], 1) < TOL[dtype]
+    # constant v: constant output
+    xc = dict(x)
+    xc["v"] = np.full_like(x["v"], x["v"].flat[0])
+    c = float(x["v64"].flat[0])
+    o = _run_prefill(xc, 3, 4.0, dtype, out_dtype=torch.float32)
+    assert np.max(np.abs(to_f64(o) - c)) < TOL[dtype] * abs(c)
+
+
+@pytest.mark.parametrize("N", [64, 256])
+def test_selectivity_end_to_end(N):
+    # posfloor, "The sqrt(N) selectivity tax": a target at the predicted
+    # alignment against N-1 distractors at the floor gets weight 0.5.
+    d, dv = 16, 16
+    t_star = T.required_alignment_based(N, 0.5)
+    q = np.zeros((1, 1, N, d), np.float32)
+    q[..., 0] = 1
+    k = np.zeros((1, 1, N, d), np.float32)
+    k[..., 0] = -1
+    k[0, 0, 0, 0] = t_star
+    v = np.zeros((1, 1, N, dv), np.float32)
+    v[0, 0, 0, 0] = 1
+    say("selectivity", N)
+    o = tl.prefill(to_device(q, "f32"), to_device(k, "f32"), to_device(v, "f32"), 3, 1.0)
+    torch.cuda.synchronize()
+    got = float(o[0, 0, N - 1, 0])
+    ref = T.direct(q[0, 0].astype(np.float64), k[0, 0].astype(np.float64), v[0, 0].astype(np.float64),
+                   3, 1.0, rows=[N - 1])[0, 0]
+    assert abs(ref - 0.5) < 1e-6  # fp32-rounded t* moves the exact weight a little
+    assert abs(got - 0.5) < 1e-4
+
+
+@pytest.mark.parametrize("d,dv,n", CONFIGS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_after_prefill(d, dv, n, dtype):
+    B, H, N, steps = 2, 3, 150, 5
+    a = math.sqrt(d)
+    x = _inputs(B, H, N + steps, d, dv, dtype, 55, _qk_kind(d, n))
+    q, k, v = (to_device(x[s], dtype) for s in "qkv")
+    say("decode", d, dv, n, dtype)
+    _, S, z = tl.prefill(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(), n, a,
+                         want_output=False, return_state=True)
+    outs = []
+    for s in range(steps):
+        t = N + s
+        outs.append(tl.decode(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                              S, z, n, a, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    got = np.stack([to_f64(o_) for o_ in outs], axis=2)
+    ref = T.direct(x["q64"], x["k64"], x["v64"], n, a, rows=list(range(N, N + steps)))
+    err = normwise_rel(got, ref)
+    say("  err", err)
+    assert err < TOL[dtype]
+    Sr, zr = T.state(x["k64"], x["v64"], n)
+    assert normwise_rel(to_f64(S), Sr) < TOL[dtype]
+
+
+def test_decode_from_oracle_state():
+    # decode alone, starting from a state the oracle computed
+    d, dv, n, a, N = 16, 64, 3, 4.0, 500
+    x = _inputs(1, 4, N + 1, d, dv, "f32", 77)
+    S0, z0 = T.state(x["k64"][:, :, :N], x["v64"][:, :, :N], n)
+    S = torch.from_numpy(S0.astype(np.float32)).cuda()
+    z = torch.from_numpy(z0.astype(np.float32)).cuda()
+    say("decode from oracle state")
+    o = tl.decode(to_device(x["q"][:, :, N], "f32"), to_device(x["k"][:, :, N], "f32"),
+                  to_device(x["v"][:, :, N], "f32"), S, z, n, a)
+    torch.cuda.synchronize()
+    ref = T.direct(x["q64"], x["k64"], x["v64"], n, a, rows=[N])[:, :, 0]
+    assert normwise_rel(to_f64(o)[:, :, None], ref[:, :, None]) < 1e-4
+
+
+@pytest.mark.parametrize("d,dv,n", [(16, 64, 3), (16, 64, 5)])
+def test_prefill_deterministic(d, dv, n):
+    x = _inputs(2, 2, 1500, d, dv, "bf16", 91, _qk_kind(d, n))
+    say("determinism", d, dv, n)
+    o1 = _run_prefill(x, n, 4.0, "bf16")
+    o2 = _run_prefill(x, n, 4.0, "bf16")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_bf16_output_matches_fp32_output():
+    x = _inputs(1, 2, 333, 16, 64, "bf16", 5)
+    say("bf16 vs fp32 output")
+    o32 = _run_prefill(x, 3, 4.0, "bf16", out_dtype=torch.float32)
+    o16 = _run_prefill(x, 3, 4.0, "bf16", out_dtype=torch.bfloat16)
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
