@@ -1,0 +1,258 @@
+"""Benchmark: causal Taylor-series linear attention on one MI355X.
+
+One "step" is one taylor_attn_prefill call over the Based-style order-2
+workload (B=4, H=16, N=4096, d=16 -> 153 symmetric features, dv=64, bf16 in
+and out, fp32 accumulation, a = sqrt(d)): feature maps, score tiles,
+read-out, intra-chunk term, state update and normalisation all run inside
+that call. Inputs rotate over several resident replicas whose total exceeds
+the 256 MiB last-level cache, so every step reads them from HBM.
+
+Printed: ONE JSON line with the prefill throughput (tokens/s) and its MFMA
+fraction, the decode state bandwidth of the order-2 decode workload (64 x 16
+heads, states seeded by a 32768-token prefill) as a fraction of HBM peak, the
+roofline of the dominant kernel and the fp64 CPU oracle timed beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       [--no-decode] [--only prefill|decode|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FP32_DENSE_TFLOPS = 157.3
+PREFILL = "based_order2_prefill"
+DECODE = "order2_decode"
+CHUNK = 64                      # tokens per chunk of the order-2 d=16 kernels
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_prefill(w, chunk=CHUNK):
+    """Per-call algorithmic bytes and flops.
+
+    bytes: q, k, v read once and o written once: (2d + dv) * in + dv * out.
+    flops: 4 F (dv+1) for state read-out and update (with the denominator
+    column) + (min(c,256)+1)(d+dv+1) for the causal half of the diagonal block.
+    """
+    from oracle.taylor_oracle import n_features  # width formula only
+    F = n_features(w.d, w.n_terms)
+    esz = 2 if w.dtype == "bf16" else 4
+    th = w.B * w.H * w.N
+    bytes_ = th * ((2 * w.d + w.dv) * esz + w.dv * esz)
+    flops = th * (4 * F * (w.dv + 1) + (min(chunk, 256) + 1) * (w.d + w.dv + 1))
+    return bytes_, flops, F
+
+
+def dev_tensor(arr, dtype, torch):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def time_loop(fn, steps, torch):
+    """Average ms per call over `steps` calls, with HIP events on the current stream."""
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_prefill(args, torch, tl, W):
+    w = W.WORKLOADS[PREFILL]
+    x = W.make_workload(w)
+    reps = args.replicas
+    qs = [dev_tensor(x["q"], w.dtype, torch) for _ in range(reps)]
+    ks = [dev_tensor(x["k"], w.dtype, torch) for _ in range(reps)]
+    vs = [dev_tensor(x["v"], w.dtype, torch) for _ in range(reps)]
+    os_ = [torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device="cuda") for _ in range(reps)]
+    ws_bytes = tl.prefill_workspace_bytes(w.B, w.H, w.N, w.d, w.dv, w.n_terms, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    L = tl.lib()
+
+    def step(i):
+        r = i % reps
+        st = L.taylor_attn_prefill(
+            tl._ptr(qs[r]), tl._ptr(ks[r]), tl._ptr(vs[r]), tl.TAYLOR_BF16, w.B, w.H, w.N, w.d, w.dv,
+            w.n_terms, w.a, None, None, tl._ptr(os_[r]), tl.TAYLOR_BF16, None, None, tl._ptr(ws),
+            ws_bytes, tl._stream())
+        if st != 0:
+            tl.check(st)
+
+    for i in range(args.warmup):
+        step(i)
+    ms = time_loop(step, args.steps, torch)
+    bytes_, flops, F = algorithmic_prefill(w)
+    return w, ms, bytes_, flops, F, reps, x
+
+
+def bench_decode(args, torch, tl, W):
+    w = W.WORKLOADS[DECODE]
+    log("decode: generating the 32768-token seeding prefill and", w.steps, "steps")
+    x = W.make_decode_inputs(w)
+    pk = dev_tensor(x["prefill_k"], "f32", torch)
+    pv = dev_tensor(x["prefill_v"], "f32", torch)
+    _, S, z = tl.prefill(pk, pk, pv, w.n_terms, w.a, want_output=False, return_state=True)
+    torch.cuda.synchronize()
+    del pk, pv
+    R = args.decode_replicas
+    Ss = [S.clone() for _ in range(R)]
+    zs = [z.clone() for _ in range(R)]
+    sq = dev_tensor(np.moveaxis(x["step_q"], 2, 0), "f32", torch)
+    sk = dev_tensor(np.moveaxis(x["step_k"], 2, 0), "f32", torch)
+    sv = dev_tensor(np.moveaxis(x["step_v"], 2, 0), "f32", torch)
+    o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device="cuda")
+    L = tl.lib()
+
+    def make_step(R_):
+        def step(i):
+            s = i % w.steps
+            r = i % R_
+            st = L.taylor_attn_decode(tl._ptr(sq[s]), tl._ptr(sk[s]), tl._ptr(sv[s]), tl.TAYLOR_F32, w.B, w.H,
+                                      w.d, w.dv, w.n_terms, w.a, tl._ptr(Ss[r]), tl._ptr(zs[r]), tl._ptr(o),
+                                      tl.TAYLOR_F32, tl._stream())
+            if st != 0:
+                tl.check(st)
+        return step
+
+    cold = make_step(R)
+    for i in range(min(args.warmup * 4, 64)):
+        cold(i)
+    ms_cold = time_loop(cold, w.steps, torch)
+    hot = make_step(1)
+    for i in range(16):
+        hot(i)
+    ms_hot = time_loop(hot, w.steps, torch)
+    from oracle.taylor_oracle import n_features
+    F = n_features(w.d, w.n_terms)
+    state_bytes = 2 * F * (w.dv + 1) * 4 * w.B * w.H   # read + write of S and z
+    flops = 4 * F * (w.dv + 1) * w.B * w.H / 2            # 2F(dv+1) per head-step
+    return {
+        "workload": DECODE, "heads": w.B * w.H, "features": F, "steps_timed": w.steps,
+        "state_bytes_per_step": state_bytes,
+        "us_per_step_cold": ms_cold * 1e3, "us_per_step_hot": ms_hot * 1e3,
+        "state_GBps_cold": state_bytes / (ms_cold * 1e-3) / 1e9,
+        "state_GBps_hot": state_bytes / (ms_hot * 1e-3) / 1e9,
+        "hbm_frac_cold": state_bytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "state_replicas_cold": R, "algorithmic_gflop_per_step": flops / 1e9,
+        "kernel": "decode_kernel<16,64,3,fp32>",
+    }
+
+
+def cpu_baseline(w, x, budget_s):
+    """fp64 oracle direct() on the first heads of the same inputs until ~budget_s."""
+    from oracle import taylor_oracle as T
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        T.direct(x["q64"][b, h], x["k64"][b, h], x["v64"][b, h], w.n_terms, w.a)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    token_heads = done * w.N
+    return {"value": token_heads / dt / w.H, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {len(heads)} heads, all {w.N} rows each, fp64 numpy direct(); "
+                      f"tokens/s = token-heads/s / H; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--decode-replicas", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import taylor_series_linear_amd as tl
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    if args.only == "copy":
+        # plain copy of known size, for counter calibration (FETCH_SIZE / WRITE_SIZE)
+        n = 256 * 1024 * 1024 // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
+        return
+    if args.only == "decode":
+        print(json.dumps(bench_decode(args, torch, tl, W)))
+        return
+
+    w, ms, bytes_, flops, F, reps, x = bench_prefill(args, torch, tl, W)
+    tokens = w.B * w.N
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "prefill tokens/s + MFMA % peak; decode state GB/s % HBM peak (1 GPU)",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
+                   "n_terms": w.n_terms, "a": w.a, "features": F, "in": "bf16", "out": "bf16",
+                   "accumulate": "fp32", "input_replicas": reps, "seed": w.seed},
+        "token_heads_per_s": w.B * w.H * w.N / (ms * 1e-3),
+        "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_DENSE_TFLOPS,
+                 "frac": tflops / BF16_DENSE_TFLOPS, "flops_per_step": flops,
+                 "note": "algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head, c=64"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "taylor_attn_prefill call (segment-sum + main prefill kernels)",
+                     "bytes_per_launch": bytes_},
+    }
+    if args.only != "prefill" and not args.no_decode:
+        out["decode"] = bench_decode(args, torch, tl, W)
+    if not args.no_cpu and args.only is None:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

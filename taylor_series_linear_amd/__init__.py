@@ -41,6 +41,13 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m taylor_series_linear_amd.build`")
+    # torch ships its own HIP runtime (same soname, libamdhip64.so.7). Load it
+    # first so the library binds to that one instance; two runtimes in one
+    # process do not share devices, streams or allocations.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     fp = ctypes.POINTER(ctypes.c_float)

@@ -17,9 +17,23 @@ reference computes on the very numbers the device sees.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
+
+_THREADS = min(16, os.cpu_count() or 1)
+
+
+def _pmap(fn, items):
+    """Map over heads in a thread pool (the draws are per-head seeded, so the
+    result does not depend on the pool)."""
+    items = list(items)
+    if len(items) < 8:
+        return [fn(i) for i in items]
+    with ThreadPoolExecutor(_THREADS) as ex:
+        return list(ex.map(fn, items))
 
 
 @dataclass(frozen=True)
@@ -111,12 +125,9 @@ def make_qkv(B, H, N, d, dv, dtype="f32", seed=0, qk="normal", heads=None):
     sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     shp = (B, H) if heads is None else (len(sel),)
     out = {}
-    qs, ks, vs = [], [], []
-    for (b, h) in sel:
-        q, k, v = _head_draw(seed, b, h, N, d, dv, qk)
-        qs.append(q), ks.append(k), vs.append(v)
-    for name, arr, w in (("q", qs, d), ("k", ks, d), ("v", vs, dv)):
-        x = np.stack(arr).reshape(shp + (N, w)) if sel else np.zeros(shp + (N, w))
+    draws = _pmap(lambda bh: _head_draw(seed, bh[0], bh[1], N, d, dv, qk), sel)
+    for j, (name, w) in enumerate((("q", d), ("k", d), ("v", dv))):
+        x = np.stack([t[j] for t in draws]).reshape(shp + (N, w)) if sel else np.zeros(shp + (N, w))
         stored, exact = round_to(x, dtype)
         out[name] = stored
         out[name + "64"] = exact
@@ -147,13 +158,17 @@ def make_decode_inputs(w: Workload, heads=None, steps=None):
     sq = np.empty((len(sel), S, w.d), np.float32)
     sk = np.empty((len(sel), S, w.d), np.float32)
     sv = np.empty((len(sel), S, w.dv), np.float32)
-    for i, (b, h) in enumerate(sel):
+
+    def one(i):
+        b, h = sel[i]
         rng = np.random.default_rng([w.seed, b, h])
         pk[i] = rng.standard_normal((w.N, w.d))
         pv[i] = rng.standard_normal((w.N, w.dv))
         sq[i] = rng.standard_normal((S, w.d))
         sk[i] = rng.standard_normal((S, w.d))
         sv[i] = rng.standard_normal((S, w.dv))
+
+    _pmap(one, range(len(sel)))
     r = lambda x: x.reshape(shp + x.shape[1:])
     return {"prefill_k": r(pk), "prefill_v": r(pv),
             "step_q": r(sq), "step_k": r(sk), "step_v": r(sv)}
