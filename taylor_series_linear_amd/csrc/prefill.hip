@@ -31,6 +31,7 @@
 #include "internal.hpp"
 #include "mma.hpp"
 
+#include <type_traits>
 #include <utility>
 
 namespace tl {
@@ -272,6 +273,71 @@ __device__ __forceinline__ void gen_table(int w, int lane, int f0, const typenam
   }
 }
 
+
+// Score tiles of one chunk handled by wave R (tiles R, R+NW, ...): all
+// operand fragments are fetched first, then the MFMAs run, then the
+// polynomial and the causal mask are applied in registers and the P^T tile
+// (query-major, keys contiguous) is written to LDS. Tiles above the diagonal
+// inside the last 32-key step are written as zeros.
+template <class Cfg, int R>
+__device__ __forceinline__ void score_tiles(const typename Cfg::E* sK, const typename Cfg::E* sQ,
+                                            typename Cfg::E* sP, int c, int g4, float inv_a) {
+  using M = typename Cfg::M;
+  using frag = typename M::frag;
+  using half = typename M::half;
+  constexpr int NW = Cfg::NW, XP = Cfg::XP, D = Cfg::D;
+  constexpr TileList<Cfg> tiles = make_tiles<Cfg>();
+  constexpr int NTR = (Cfg::NTILES - R + NW - 1) / NW;
+  constexpr int KU = D == 16 ? 1 : D / 32;
+  using opnd = std::conditional_t<D == 16, half, frag>;
+  opnd ak[NTR > 0 ? NTR : 1][KU], bq[NTR > 0 ? NTR : 1][KU];
+  static_for<0, NTR>([&](auto ji) {
+    constexpr int j = decltype(ji)::value;
+    constexpr int kt = tiles.kt[R + j * NW], qt = tiles.qt[R + j * NW];
+    if constexpr (kt <= qt) {
+      static_for<0, KU>([&](auto ui) {
+        constexpr int u = decltype(ui)::value;
+        if constexpr (D == 16) {
+          ak[j][u] = *reinterpret_cast<const half*>(sK + (16 * kt + c) * XP + 4 * g4);
+          bq[j][u] = *reinterpret_cast<const half*>(sQ + (16 * qt + c) * XP + 4 * g4);
+        } else {
+          ak[j][u] = lds_frag8(sK + (16 * kt + c) * XP + 32 * u + 8 * g4);
+          bq[j][u] = lds_frag8(sQ + (16 * qt + c) * XP + 32 * u + 8 * g4);
+        }
+      });
+    }
+  });
+  f32x4 acc[NTR > 0 ? NTR : 1];
+  static_for<0, NTR>([&](auto ji) {
+    constexpr int j = decltype(ji)::value;
+    constexpr int kt = tiles.kt[R + j * NW], qt = tiles.qt[R + j * NW];
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kt <= qt) {
+      static_for<0, KU>([&](auto ui) {
+        constexpr int u = decltype(ui)::value;
+        if constexpr (D == 16)
+          acc[j] = M::hstep(ak[j][u], bq[j][u], acc[j]);
+        else
+          acc[j] = M::step(ak[j][u], bq[j][u], acc[j]);
+      });
+    }
+  });
+  static_for<0, NTR>([&](auto ji) {
+    constexpr int j = decltype(ji)::value;
+    constexpr int kt = tiles.kt[R + j * NW], qt = tiles.qt[R + j * NW];
+    typename Cfg::E* dst = sP + (16 * qt + c) * Cfg::PP + 16 * kt + 4 * g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float wv = 0.f;
+      if constexpr (kt <= qt) {
+        wv = taylor_poly<Cfg::NT>(acc[j][i] * inv_a);
+        if (kt == qt && 4 * g4 + i > c) wv = 0.f;  // causal mask (key > query)
+      }
+      dst[i] = M::cvt(wv);
+    }
+  });
+}
+
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
@@ -349,48 +415,95 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           S[ft][i] = val;
         }
     }
+    // sum of the earlier segments' states, PB segments' loads in flight at once
     const int PS = a.P - 1;
-    for (int pp = 0; pp < p; ++pp) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.seg) +
-                         ((((static_cast<size_t>(bh) * PS + pp) * G + gsl) * NW + w) * FT) * 64 + lane;
+    constexpr int PB = FT <= 10 ? 4 : (FT <= 20 ? 2 : 1);
+    for (int pp = 0; pp < p; pp += PB) {
+      f32x4 t[PB][FT];
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) S[ft] += src[ft * 64];
+      for (int j = 0; j < PB; ++j) {
+        // segments past p - 1 re-read segment pp (in bounds) and are dropped
+        const int ps = pp + j < p ? pp + j : pp;
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.seg) +
+                           ((((static_cast<size_t>(bh) * PS + ps) * G + gsl) * NW + w) * FT) * 64 + lane;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) t[j][ft] = src[ft * 64];
+      }
+#pragma unroll
+      for (int j = 0; j < PB; ++j)
+        if (pp + j < p) {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) S[ft] += t[j][ft];
+        }
     }
   }
 
   const float inv_a = a.inv_a;
 
   // ---- chunk loop ------------------------------------------------------------
+  // Global loads run one chunk ahead: the next chunk's Q, K and V rows are
+  // fetched into registers (16 bytes per item) while the current chunk is in
+  // compute, then written to LDS at the top of the next iteration.
+  constexpr int EV = 16 / Cfg::ES;         // elements per 16-byte item
+  constexpr int NQI = C * D / EV;          // items of Q (and of K)
+  constexpr int NVI = C * DV / EV;         // items of V
+  constexpr int QB = MAIN ? NQI : 0;       // Q items exist only when reading out
+  constexpr int NIT = QB + NQI + NVI;
+  constexpr int NSLOT = (NIT + Cfg::NTHR - 1) / Cfg::NTHR;
+  uint4 pf[NSLOT];
+
+  auto fetch = [&](int cc0) {
+    const int nvv = min(C, t1 - cc0);
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const int i = tid + s * Cfg::NTHR;
+      pf[s] = uint4{0, 0, 0, 0};
+      if (i < QB) {
+        const int row = i / (D / EV), col = (i % (D / EV)) * EV;
+        if (want_out && row < nvv)
+          pf[s] = *reinterpret_cast<const uint4*>(qh + static_cast<size_t>(cc0 + row) * D + col);
+      } else if (i < QB + NQI) {
+        const int j = i - QB;
+        const int row = j / (D / EV), col = (j % (D / EV)) * EV;
+        if (row < nvv) pf[s] = *reinterpret_cast<const uint4*>(kh + static_cast<size_t>(cc0 + row) * D + col);
+      } else if (i < NIT) {
+        const int j = i - QB - NQI;
+        const int row = j / (DV / EV), col = (j % (DV / EV)) * EV;
+        if (row < nvv) pf[s] = *reinterpret_cast<const uint4*>(vh + static_cast<size_t>(cc0 + row) * DV + col);
+      }
+    }
+  };
+  // Q, K row-major; V transposed (key-contiguous) with the ones row below it.
+  auto stage = [&](int nvv) {
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const int i = tid + s * Cfg::NTHR;
+      if (i < QB) {
+        const int row = i / (D / EV), col = (i % (D / EV)) * EV;
+        if (want_out) *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = pf[s];
+      } else if (i < QB + NQI) {
+        const int j = i - QB;
+        const int row = j / (D / EV), col = (j % (D / EV)) * EV;
+        *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = pf[s];
+      } else if (i < NIT) {
+        const int j = i - QB - NQI;
+        const int row = j / (DV / EV), col = (j % (DV / EV)) * EV;
+        const E* e = reinterpret_cast<const E*>(&pf[s]);
+#pragma unroll
+        for (int u = 0; u < EV; ++u) sV[(col + u) * Cfg::PK + row] = e[u];
+      }
+    }
+    for (int i = tid; i < C; i += Cfg::NTHR) sV[DV * Cfg::PK + i] = M::cvt(i < nvv ? 1.f : 0.f);
+  };
+
+  if (t0 < t1) fetch(t0);
   for (int c0 = t0; c0 < t1; c0 += C) {
     const int nv = min(C, t1 - c0);
     const bool last_chunk = c0 + C >= t1;
     const bool do_update = !MAIN || !last_chunk || want_state;
 
-    // stage Q, K (row-major) and V^T (+ ones row) in LDS
-    {
-      constexpr int EV = 16 / Cfg::ES;   // elements per 16-byte vector
-      constexpr int VPR = D / EV;        // vectors per q/k row
-      for (int i = tid; i < C * VPR; i += Cfg::NTHR) {
-        const int row = i / VPR, col = (i % VPR) * EV;
-        uint4 vk = {0, 0, 0, 0}, vq = {0, 0, 0, 0};
-        if (row < nv) {
-          vk = *reinterpret_cast<const uint4*>(kh + static_cast<size_t>(c0 + row) * D + col);
-          if (want_out) vq = *reinterpret_cast<const uint4*>(qh + static_cast<size_t>(c0 + row) * D + col);
-        }
-        *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = vk;
-        if (want_out) *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = vq;
-      }
-      constexpr int VPRV = DV / EV;
-      for (int i = tid; i < C * VPRV; i += Cfg::NTHR) {
-        const int row = i / VPRV, col = (i % VPRV) * EV;
-        uint4 vv = {0, 0, 0, 0};
-        if (row < nv) vv = *reinterpret_cast<const uint4*>(vh + static_cast<size_t>(c0 + row) * DV + col);
-        const E* e = reinterpret_cast<const E*>(&vv);
-#pragma unroll
-        for (int j = 0; j < EV; ++j) sV[(col + j) * Cfg::PK + row] = e[j];
-      }
-      for (int i = tid; i < C; i += Cfg::NTHR) sV[DV * Cfg::PK + i] = M::cvt(i < nv ? 1.f : 0.f);
-    }
+    stage(nv);
+    if (!last_chunk) fetch(c0 + C);
     __syncthreads();
 
     // features and score tiles
@@ -413,47 +526,34 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       if (do_update) gen_table<Cfg, false>(w, lane, f0, sK, sPK, inv_a);
     }
     if (want_out && gsl == 0) {
-      constexpr TileList<Cfg> tiles = make_tiles<Cfg>();
-      static_for<0, Cfg::NTILES>([&](auto tii) {
-        constexpr int ti = decltype(tii)::value;
-        constexpr int kt = tiles.kt[ti], qt = tiles.qt[ti];
-        if (ti % NW == w) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (kt <= qt) {
-            if constexpr (D == 16) {
-              const auto ak = *reinterpret_cast<const typename M::half*>(sK + (16 * kt + c) * Cfg::XP + 4 * g4);
-              const auto bq = *reinterpret_cast<const typename M::half*>(sQ + (16 * qt + c) * Cfg::XP + 4 * g4);
-              acc = M::hstep(ak, bq, acc);
-            } else {
-#pragma unroll
-              for (int u = 0; u < D / 32; ++u) {
-                const frag ak = lds_frag8(sK + (16 * kt + c) * Cfg::XP + 32 * u + 8 * g4);
-                const frag bq = lds_frag8(sQ + (16 * qt + c) * Cfg::XP + 32 * u + 8 * g4);
-                acc = M::step(ak, bq, acc);
-              }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float wv = taylor_poly<Cfg::NT>(acc[i] * inv_a);
-              if (kt == qt && 4 * g4 + i > c) wv = 0.f;  // causal mask (key > query)
-              acc[i] = wv;
-            }
-          }
-          E* dst = sP + (16 * qt + c) * Cfg::PP + 16 * kt + 4 * g4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = M::cvt(acc[i]);
-        }
+      static_for<0, NW>([&](auto ri) {
+        if (w == decltype(ri)::value) score_tiles<Cfg, decltype(ri)::value>(sK, sQ, sP, c, g4, inv_a);
       });
     }
     __syncthreads();
 
+    // [V,1]^T fragments of this wave's dv tile (A operand of the intra-chunk
+    // term, B operand of the state update).
+    frag bv[KSC];
+#pragma unroll
+    for (int u = 0; u < KSC; ++u) bv[u] = lds_frag8(sV + (16 * w + c) * Cfg::PK + 32 * u + 8 * g4);
+
     if (want_out) {
-      // read-out of the state: O^T[dv tile w] = S^T phi~(Q)^T
+      // read-out of the state: O^T[dv tile w] = S^T phi~(Q)^T. The phi~(Q)
+      // fragments of k-step t+1 are fetched before the MFMAs of k-step t.
       f32x4 acc[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      frag bq[2][QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) bq[0][qt] = lds_frag_split(sPQ + (16 * qt + c) * Cfg::PQ + 4 * g4);
 #pragma unroll
       for (int t = 0; t < KSF; ++t) {
+        if (t + 1 < KSF) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            bq[(t + 1) & 1][qt] = lds_frag_split(sPQ + (16 * qt + c) * Cfg::PQ + 32 * (t + 1) + 4 * g4);
+        }
         frag sa;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -461,21 +561,33 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           sa[j + 4] = M::cvt(S[2 * t + 1][j]);
         }
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const frag bq = lds_frag_split(sPQ + (16 * qt + c) * Cfg::PQ + 32 * t + 4 * g4);
-          acc[qt] = M::step(sa, bq, acc[qt]);
-        }
+        for (int qt = 0; qt < QT; ++qt) acc[qt] = M::step(sa, bq[t & 1][qt], acc[qt]);
       }
-      // intra-chunk term: O^T += [V,1]^T P^T (first slice only)
+      // intra-chunk term: O^T += [V,1]^T P^T (first slice only); all P^T
+      // fragments are fetched before the MFMAs.
       if (gsl == 0) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int u = 0; u <= qt / 2; ++u) {
-            const frag av = lds_frag8(sV + (16 * w + c) * Cfg::PK + 32 * u + 8 * g4);
-            const frag bp = lds_frag8(sP + (16 * qt + c) * Cfg::PP + 32 * u + 8 * g4);
-            acc[qt] = M::step(av, bp, acc[qt]);
-          }
+        constexpr int NPF = [] {
+          int n = 0;
+          for (int qt = 0; qt < QT; ++qt) n += qt / 2 + 1;
+          return n;
+        }();
+        frag bp[NPF];
+        static_for<0, QT>([&](auto qi) {
+          constexpr int qt = decltype(qi)::value;
+          constexpr int base = [] { int n = 0; for (int q2 = 0; q2 < qt; ++q2) n += q2 / 2 + 1; return n; }();
+          static_for<0, qt / 2 + 1>([&](auto ui) {
+            constexpr int u = decltype(ui)::value;
+            bp[base + u] = lds_frag8(sP + (16 * qt + c) * Cfg::PP + 32 * u + 8 * g4);
+          });
+        });
+        static_for<0, QT>([&](auto qi) {
+          constexpr int qt = decltype(qi)::value;
+          constexpr int base = [] { int n = 0; for (int q2 = 0; q2 < qt; ++q2) n += q2 / 2 + 1; return n; }();
+          static_for<0, qt / 2 + 1>([&](auto ui) {
+            constexpr int u = decltype(ui)::value;
+            acc[qt] = M::step(bv[u], bp[base + u], acc[qt]);
+          });
+        });
       }
       if constexpr (G == 1) {
         // denominator: row DV of O^T = wave NW-1, lane group 0, element 0
@@ -518,15 +630,21 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     }
 
     if (do_update) {
-      // S[:, dv tile w] += phi(K)^T [V,1][:, dv tile w]
+      // S[:, dv tile w] += phi(K)^T [V,1][:, dv tile w]; the phi(K)^T
+      // fragments of feature tile ft+1 are fetched before the MFMAs of ft.
+      frag ak[2][KSC];
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
+      for (int u = 0; u < KSC; ++u) ak[0][u] = lds_frag8(sPK + c * Cfg::PK + 32 * u + 8 * g4);
 #pragma unroll
-        for (int u = 0; u < KSC; ++u) {
-          const frag ak = lds_frag8(sPK + (16 * ft + c) * Cfg::PK + 32 * u + 8 * g4);
-          const frag bv = lds_frag8(sV + (16 * w + c) * Cfg::PK + 32 * u + 8 * g4);
-          S[ft] = M::step(ak, bv, S[ft]);
+      for (int ft = 0; ft < FT; ++ft) {
+        if (ft + 1 < FT) {
+#pragma unroll
+          for (int u = 0; u < KSC; ++u)
+            ak[(ft + 1) & 1][u] = lds_frag8(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
         }
+#pragma unroll
+        for (int u = 0; u < KSC; ++u) S[ft] = M::step(ak[ft & 1][u], bv[u], S[ft]);
+      }
     }
     __syncthreads();
   }
