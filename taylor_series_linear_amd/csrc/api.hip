@@ -64,54 +64,14 @@ int64_t checked_mul(std::initializer_list<int64_t> xs) {
   return r;
 }
 
-struct Plan {
-  tl::PrefillTraits t;
-  int P = 1;
-  int L = 0;
-  size_t seg_off = 0, fin_off = 0, part_off = 0, bytes = 0;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-// Sequence split: enough workgroups (heads x segments x slices) to give each
-// compute unit about two, and at least 4 chunks per segment.
-void plan_prefill(int BH, int N, int dv, const tl::PrefillTraits& t, Plan* p) {
-  p->t = t;
-  const int C = t.C;
-  const int64_t nchunks = (static_cast<int64_t>(N) + C - 1) / C;
-  if (BH <= 0 || nchunks == 0) {
-    p->P = 1;
-    p->L = N;
-    p->bytes = 0;
-    return;
-  }
-  const int64_t target = 512;
-  int64_t want = (target + static_cast<int64_t>(BH) * t.G - 1) / (static_cast<int64_t>(BH) * t.G);
-  int64_t maxp = nchunks / 4 > 1 ? nchunks / 4 : 1;
-  int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
-  const int64_t cps = (nchunks + P - 1) / P;
-  p->L = static_cast<int>(cps * C);
-  p->P = static_cast<int>((nchunks + cps - 1) / cps);
-  const int DVP = t.NW * 16;
-  const size_t FP = static_cast<size_t>(t.G) * t.FS;
-  size_t off = 0;
-  p->seg_off = off;
-  if (p->P > 1) off += align256(static_cast<size_t>(BH) * (p->P - 1) * FP * DVP * 4);
-  p->fin_off = off;
-  if (p->P > 1) off += align256(static_cast<size_t>(BH) * FP * DVP * 4);
-  p->part_off = off;
-  if (t.G > 1) off += align256(static_cast<size_t>(t.G) * BH * static_cast<size_t>(N) * (dv + 4) * 4);
-  p->bytes = off;
-}
-
 taylor_status hip_status(hipError_t e, const char* where) {
   if (e == hipSuccess) return TAYLOR_OK;
   return fail(TAYLOR_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
-// Validation shared by the size query and the call.
+// Validation shared by the size query and the call; fills the plan.
 taylor_status check_prefill_shape(int B, int H, int N, int d, int dv, int n_terms,
-                                  taylor_dtype in_dtype, tl::PrefillTraits* t) {
+                                  taylor_dtype in_dtype, tl::PrefillPlan* plan) {
   taylor_status s = check_dtype(in_dtype, "in_dtype");
   if (s != TAYLOR_OK) return s;
   if (B < 0 || H < 0 || N < 0)
@@ -119,7 +79,7 @@ taylor_status check_prefill_shape(int B, int H, int N, int d, int dv, int n_term
   if ((s = check_dn(d, dv, n_terms, true)) != TAYLOR_OK) return s;
   if (checked_mul({B, H, N, d > dv ? d : dv}) < 0 || checked_mul({B, H}) > INT32_MAX / 64)
     return fail(TAYLOR_ERR_BAD_SHAPE, "B*H*N*max(d,dv) overflows");
-  if (!tl::prefill_traits(d, dv, n_terms, in_dtype == TAYLOR_BF16, t))
+  if (!tl::prefill_plan(d, dv, n_terms, in_dtype == TAYLOR_BF16, B * H, N, plan))
     return fail(TAYLOR_ERR_UNSUPPORTED, "no prefill instantiation for this configuration");
   return TAYLOR_OK;
 }
@@ -174,10 +134,8 @@ taylor_status taylor_feature_map(const void* x, taylor_dtype x_dtype, int64_t ro
 
 size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_terms,
                                      taylor_dtype in_dtype) {
-  tl::PrefillTraits t;
-  if (check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &t) != TAYLOR_OK) return static_cast<size_t>(-1);
-  Plan p;
-  plan_prefill(B * H, N, dv, t, &p);
+  tl::PrefillPlan p;
+  if (check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &p) != TAYLOR_OK) return static_cast<size_t>(-1);
   return p.bytes;
 }
 
@@ -186,8 +144,8 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   int n_terms, float a, const float* S0, const float* z0,
                                   void* o, taylor_dtype out_dtype, float* S, float* z,
                                   void* workspace, size_t ws_bytes, void* stream) {
-  tl::PrefillTraits t;
-  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &t);
+  tl::PrefillPlan p;
+  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &p);
   if (s != TAYLOR_OK) return s;
   if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
   if ((s = check_scale(a)) != TAYLOR_OK) return s;
@@ -198,8 +156,6 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
   const int BH = B * H;
   if (BH > 0 && N > 0 && (q == nullptr || k == nullptr || v == nullptr))
     return fail(TAYLOR_ERR_NULL_PTR, "q, k and v are required");
-  Plan p;
-  plan_prefill(BH, N, dv, t, &p);
   if (p.bytes > 0 && (workspace == nullptr || ws_bytes < p.bytes))
     return fail(TAYLOR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.bytes) +
                                           " bytes, got " + std::to_string(ws_bytes));
@@ -208,7 +164,8 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
   (void)hipGetLastError();  // report only errors of the launches below
   if (N == 0) {
     if (S == nullptr) return TAYLOR_OK;
-    return hip_status(tl::state_init_launch(S0, z0, S, z, BH, t.F, dv, st), "state init launch");
+    return hip_status(tl::state_init_launch(S0, z0, S, z, BH, static_cast<int>(taylor_feature_dim(d, n_terms)), dv, st),
+                      "state init launch");
   }
   tl::PrefillArgs args{};
   args.q = q;
@@ -223,7 +180,7 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
   char* ws = static_cast<char*>(workspace);
   args.seg = p.P > 1 ? reinterpret_cast<float*>(ws + p.seg_off) : nullptr;
   args.fin = p.P > 1 ? reinterpret_cast<float*>(ws + p.fin_off) : nullptr;
-  args.part = t.G > 1 ? reinterpret_cast<float*>(ws + p.part_off) : nullptr;
+  args.part = p.bytes > p.part_off ? reinterpret_cast<float*>(ws + p.part_off) : nullptr;
   args.BH = BH;
   args.N = N;
   args.P = p.P;

@@ -7,13 +7,14 @@
 
 namespace tl {
 
-// Launch geometry of one prefill instantiation, known to the host.
-struct PrefillTraits {
-  int F;    // features
-  int FS;   // features per slice (one workgroup's share of the state)
-  int G;    // slices
-  int C;    // tokens per chunk
-  int NW;   // waves per workgroup (dv tiles incl. the denominator tile)
+// Sequence split and workspace layout of one prefill call.
+struct PrefillPlan {
+  int P = 1;             // segments per head
+  int L = 0;             // tokens per segment (multiple of the chunk length)
+  size_t seg_off = 0;    // byte offsets into the workspace
+  size_t fin_off = 0;
+  size_t part_off = 0;
+  size_t bytes = 0;      // workspace size
 };
 
 struct PrefillArgs {
@@ -26,9 +27,9 @@ struct PrefillArgs {
   int out_bf16;
   float* S;
   float* z;
-  float* seg;   // segment sums, [BH][P-1][G][NW][FS/16][64] x float4
-  float* fin;   // final state staging, [BH][G][NW][FS/16][64] x float4 (defer_state)
-  float* part;  // partial outputs, [G][BH][N][DV+4] (G > 1 only)
+  float* seg;   // per-segment state sums (layout private to the kernel family)
+  float* fin;   // final-state staging for in-place continuation (defer_state)
+  float* part;  // partial outputs of feature-sliced kernels
   int BH;
   int N;
   int P;        // segments per head
@@ -37,8 +38,9 @@ struct PrefillArgs {
   int defer_state;  // final state goes through `fin`, then a copy kernel
 };
 
-// Returns false when (d, dv, n_terms, bf16) is not instantiated.
-bool prefill_traits(int d, int dv, int n_terms, bool bf16, PrefillTraits* t);
+// Plans a prefill of BH heads x N tokens. Returns false when
+// (d, dv, n_terms, bf16) is not instantiated.
+bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillPlan* plan);
 
 // Enqueue the whole prefill for one instantiation. Returns hipSuccess or the
 // launch error.
@@ -47,6 +49,12 @@ hipError_t prefill_launch(int d, int dv, int n_terms, bool bf16, const PrefillAr
 
 hipError_t state_init_launch(const float* S0, const float* z0, float* S, float* z,
                              int64_t BH, int F, int dv, hipStream_t stream);
+
+// Order-2, d = 16, dv = 64, bf16 prefill (prefill_o2.hip).
+namespace o2 {
+bool plan(int BH, int N, PrefillPlan* plan);
+hipError_t launch(const PrefillArgs& a, hipStream_t stream);
+}  // namespace o2
 
 struct DecodeArgs {
   const void* q;

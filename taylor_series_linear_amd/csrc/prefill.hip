@@ -782,7 +782,6 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(16, 64, 1, false, 32, 64, true)         \
   X(16, 16, 3, true, 160, 64, true)         \
   X(16, 16, 3, false, 160, 64, true)        \
-  X(16, 64, 3, true, 160, 64, true)         \
   X(16, 64, 3, false, 160, 64, true)        \
   X(16, 16, 5, true, 608, 32, false)        \
   X(16, 16, 5, false, 256, 32, false)       \
@@ -797,11 +796,47 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(64, 64, 3, true, 544, 32, false)        \
   X(64, 64, 3, false, 128, 32, false)
 
-bool prefill_traits(int d, int dv, int n_terms, bool bf16, PrefillTraits* t) {
+// Sequence split for the generic kernels: enough workgroups (heads x
+// segments x slices) to give each compute unit about two, and at least 4
+// chunks per segment.
+template <class Cfg>
+static void plan_cfg(int BH, int N, PrefillPlan* p) {
+  constexpr int C = Cfg::C;
+  const int64_t nchunks = (static_cast<int64_t>(N) + C - 1) / C;
+  *p = PrefillPlan{};
+  if (BH <= 0 || nchunks == 0) {
+    p->P = 1;
+    p->L = N;
+    return;
+  }
+  const int64_t target = 512;
+  const int64_t want = (target + static_cast<int64_t>(BH) * Cfg::G - 1) / (static_cast<int64_t>(BH) * Cfg::G);
+  const int64_t maxp = nchunks / 4 > 1 ? nchunks / 4 : 1;
+  const int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
+  const int64_t cps = (nchunks + P - 1) / P;
+  p->L = static_cast<int>(cps * C);
+  p->P = static_cast<int>((nchunks + cps - 1) / cps);
+  const size_t FP = static_cast<size_t>(Cfg::G) * Cfg::FS;
+  auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  size_t off = 0;
+  p->seg_off = off;
+  if (p->P > 1) off += al(static_cast<size_t>(BH) * (p->P - 1) * FP * Cfg::DVP * 4);
+  p->fin_off = off;
+  if (p->P > 1) off += al(static_cast<size_t>(BH) * FP * Cfg::DVP * 4);
+  p->part_off = off;
+  if (Cfg::G > 1) off += al(static_cast<size_t>(Cfg::G) * BH * static_cast<size_t>(N) * Cfg::PPITCH * 4);
+  p->bytes = off;
+}
+
+static bool is_o2(int d, int dv, int n_terms, bool bf16) {
+  return d == 16 && dv == 64 && n_terms == 3 && bf16;
+}
+
+bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillPlan* plan) {
+  if (is_o2(d, dv, n_terms, bf16)) return o2::plan(BH, N, plan);
 #define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
   if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_) {             \
-    using Cf = PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>;                      \
-    *t = PrefillTraits{Cf::F, Cf::FS, Cf::G, Cf::C, Cf::NW};               \
+    plan_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(BH, N, plan);          \
     return true;                                                           \
   }
   TL_PREFILL_CFGS(X)
@@ -811,6 +846,7 @@ bool prefill_traits(int d, int dv, int n_terms, bool bf16, PrefillTraits* t) {
 
 hipError_t prefill_launch(int d, int dv, int n_terms, bool bf16, const PrefillArgs& a,
                           hipStream_t stream) {
+  if (is_o2(d, dv, n_terms, bf16)) return o2::launch(a, stream);
 #define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
   if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_)               \
     return launch_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(a, stream);
