@@ -34,7 +34,80 @@ BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 FP32_DENSE_TFLOPS = 157.3
 PREFILL = "based_order2_prefill"
 DECODE = "order2_decode"
-CHUNK = 64                      # tokens per chunk of the order-2 d=16 kernels
+CHUNK = 32                      # tokens per chunk of the order-2 d=16 bf16 kernel
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic_based_order2_prefill.json")
+
+
+def source_hash():
+    """Hash of the HIP sources, to tell whether stored counter data still
+    describes the kernels being timed."""
+    import hashlib
+    csrc = os.path.join(ROOT, "taylor_series_linear_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE of the prefill
+    bench; the same two counters over bench.py --only copy) into per-call HBM
+    bytes. The counters report KiB per dispatch; each is scaled by the ratio
+    of the plain copy's known bytes to what the same counter reads for it."""
+    copy_bytes = 256 * 1024 * 1024
+
+    def per_kernel(rows, counter):
+        acc = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    f_copy = per_kernel(_pmc_rows(copy_fetch_dir), "FETCH_SIZE")
+    w_copy = per_kernel(_pmc_rows(copy_write_dir), "WRITE_SIZE")
+    ck = max(f_copy, key=lambda k: f_copy[k])      # the 256 MiB copy kernel
+    f_scale = copy_bytes / f_copy[ck]
+    w_scale = copy_bytes / w_copy[max(w_copy, key=lambda k: w_copy[k])]
+    fetch = per_kernel(_pmc_rows(fetch_dir), "FETCH_SIZE")
+    write = per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        if "o2_" not in k and "prefill" not in k:
+            continue
+        kernels[k] = {"fetch_bytes": fetch.get(k, 0.0) * f_scale, "write_bytes": write.get(k, 0.0) * w_scale}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
+    rec = {"workload": PREFILL, "source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_kernel": ck, "kernels": kernels, "bytes_per_call": total}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def stored_traffic():
+    """HBM bytes per prefill call from the stored counter summary, or None if
+    the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC) as f:
+            rec = json.load(f)
+    except OSError:
+        return None
+    return rec["bytes_per_call"] if rec.get("source_hash") == source_hash() else None
 
 
 def log(*a):
@@ -191,7 +264,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="summarise rocprofv3 --pmc runs into the stored traffic record and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, TRAFFIC)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -241,11 +319,11 @@ def main():
         "token_heads_per_s": w.B * w.H * w.N / (ms * 1e-3),
         "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_DENSE_TFLOPS,
                  "frac": tflops / BF16_DENSE_TFLOPS, "flops_per_step": flops,
-                 "note": "algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head, c=64"},
+                 "note": "algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head, c=32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "taylor_attn_prefill call (segment-sum + main prefill kernels)",
-                     "bytes_per_launch": bytes_},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(),
+                     "kernel": "one taylor_attn_prefill call: o2 segment sums + prefix scan + main (3 launches)",
+                     "launch_us": ms * 1e3, "algorithmic_bytes_per_launch": bytes_},
     }
     if args.only != "prefill" and not args.no_decode:
         out["decode"] = bench_decode(args, torch, tl, W)
