@@ -124,6 +124,11 @@ size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_t
  * B, H or N may be 0: then no token is processed; with N = 0 the final state
  * is S0 (or zero). The normalisation divides by a sum of weights that is
  * >= 1/2 per key for n_terms = 3 (>= 0.27 for 5), so it never divides by 0.
+ * Range: the bf16 order-2 d = 16 dv = 64 instantiation carries keys, values,
+ * key products k_i k_j and the weights w(q.k/a) in fp16 inside its state
+ * update and intra-chunk term (fp32 accumulation), so |k_i k_j|, |v| and
+ * w(q.k/a) must stay below 65504; under the normalisation the method asks for
+ * (|q.k/a| of order 1) this always holds.
  */
 taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   taylor_dtype in_dtype, int B, int H, int N, int d, int dv,

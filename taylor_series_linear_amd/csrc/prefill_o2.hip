@@ -30,13 +30,19 @@
 // zero) and its read-out uses a hi/lo bf16 split so the count z_0 is not
 // rounded to 8 bits.
 //
+// Precision: scores and the read-out use bf16 operands; the state update,
+// the intra-chunk term and Z use fp16 operands (keys, values, key products
+// and weights are exact or better than bf16 in fp16 within its range), all
+// with fp32 accumulation and fp32 states.
+//
 // Work decomposition: one workgroup of 4 waves per (head, segment).
 //  * waves 0, 1 ("M"): state columns [32m, 32m+32) of S (5 tiles of
 //    32x32 fp32 in registers); per chunk: score tile, polynomial and causal
 //    mask in registers, read-out, intra-chunk term, normalisation, update.
 //  * wave 2 ("Q"): stages Q, builds phi~(Q) tiles, owns Z, computes the
 //    inter-chunk denominator, stores the normalised output rows.
-//  * wave 3 ("K"): stages K, K'^T and V^T, builds phi(K)^T tiles.
+//  * wave 3 ("K"): stages K, K'^T and V^T (fp16), builds phi(K)^T tiles
+//    with packed fp16 products.
 // The Q and K waves prepare chunk c+1 in one LDS buffer while the M waves
 // consume chunk c from the other; one barrier per chunk. Global loads run
 // PD chunks ahead in registers. Segments of a head are independent given
@@ -67,14 +73,14 @@ constexpr float kSqrt2 = 1.41421356237309515f;
 // LDS layout (bf16 elements per row, 16 bytes of padding per row).
 constexpr int QP_P = 40;     // Q' rows: q[0..15], 1, zeros
 constexpr int K_P = 24;      // K rows
-constexpr int KT_P = 40;     // K'^T rows 0..31 (16 = valid-key indicator, 17.. = 0)
-constexpr int VT_P = 40;     // V^T rows
+constexpr int KF_P = 40;     // K'^T rows 0..17 in fp16 (16 = valid-key indicator, 17 = 0)
+constexpr int VT_P = 40;     // V^T rows, fp16
 constexpr int FQ_P = 168;    // phi~(Q), operand order
 constexpr int FK_P = 40;     // phi(K)^T rows
 constexpr int OFF_QP = 0;
 constexpr int OFF_K = OFF_QP + C * QP_P * 2;
 constexpr int OFF_KT = OFF_K + C * K_P * 2;
-constexpr int OFF_VT = OFF_KT + 32 * KT_P * 2;
+constexpr int OFF_VT = OFF_KT + 18 * KF_P * 2;
 constexpr int OFF_FQ = OFF_VT + DV * VT_P * 2;
 constexpr int OFF_FK = OFF_FQ + C * FQ_P * 2;
 constexpr int BUF = OFF_FK + FI * FK_P * 2;
@@ -92,7 +98,7 @@ constexpr int lds_bytes() {
 }
 static_assert(lds_bytes<true>() <= 80 * 1024, "two workgroups per CU");
 static_assert(lds_bytes<false>() <= 80 * 1024, "two workgroups per CU");
-static_assert(OFF_K % 16 == 0 && OFF_KT % 16 == 0 && OFF_VT % 16 == 0 && OFF_FQ % 16 == 0 &&
+static_assert(OFF_K % 16 == 0 && OFF_KT % 16 == 0 && (KF_P * 2) % 16 == 0 && OFF_VT % 16 == 0 && OFF_FQ % 16 == 0 &&
                   OFF_FK % 16 == 0 && BUF % 16 == 0 && OFF_O % 16 == 0,
               "16-byte aligned regions");
 
@@ -164,12 +170,36 @@ __device__ __forceinline__ float zscale(int r, int c, float inv_a) {
 // small helpers
 // ---------------------------------------------------------------------------
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 ldh8(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
+__device__ __forceinline__ f16x4 ldh4(const _Float16* p) { return *reinterpret_cast<const f16x4*>(p); }
+__device__ __forceinline__ f16x8 cath44(f16x4 a, f16x4 b) {
+  return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// bf16 -> fp16 (exact for magnitudes in fp16's normal range)
+__device__ __forceinline__ f16x8 to_h8(bf16x8 v) {
+  f16x8 r;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r[u] = static_cast<_Float16>(static_cast<float>(v[u]));
+  return r;
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ bf16x4 ld4(const __bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ __forceinline__ f32x8 ldf8(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
 __device__ __forceinline__ void st8(__bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 
 // Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3);
@@ -198,10 +228,10 @@ struct Smem {
   char* base;
   __device__ __bf16* qp(int b) const { return reinterpret_cast<__bf16*>(base + b * BUF + OFF_QP); }
   __device__ __bf16* kr(int b) const { return reinterpret_cast<__bf16*>(base + b * BUF + OFF_K); }
-  __device__ __bf16* kt(int b) const { return reinterpret_cast<__bf16*>(base + b * BUF + OFF_KT); }
-  __device__ __bf16* vt(int b) const { return reinterpret_cast<__bf16*>(base + b * BUF + OFF_VT); }
+  __device__ _Float16* kt(int b) const { return reinterpret_cast<_Float16*>(base + b * BUF + OFF_KT); }
+  __device__ _Float16* vt(int b) const { return reinterpret_cast<_Float16*>(base + b * BUF + OFF_VT); }
   __device__ __bf16* fq(int b) const { return reinterpret_cast<__bf16*>(base + b * BUF + OFF_FQ); }
-  __device__ __bf16* fk(int b) const { return reinterpret_cast<__bf16*>(base + b * BUF + OFF_FK); }
+  __device__ _Float16* fk(int b) const { return reinterpret_cast<_Float16*>(base + b * BUF + OFF_FK); }
   __device__ float* den(int b) const { return reinterpret_cast<float*>(base + OFF_DEN) + b * C; }
   __device__ char* ostage(int m, int bytes) const { return base + OFF_O + m * bytes; }
 };
@@ -220,8 +250,11 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   constexpr int OB = OStage<OBF>::BYTES;
 
   const int tid = threadIdx.x;
-  // wave index as a scalar, so role branches are uniform
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Role of this wave (a scalar, so role branches are uniform). Workgroups
+  // of the second round on a compute unit take the roles rotated by two
+  // SIMDs, so two co-resident workgroups put an MFMA wave and a staging wave
+  // on every SIMD.
+  const int w = __builtin_amdgcn_readfirstlane(((tid >> 6) + 2 * ((blockIdx.x >> 8) & 1)) & 3);
   const int l = tid & 63;
   const int lc = l & 31;
   const int lh = l >> 5;
@@ -245,15 +278,12 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   const __bf16* vh = reinterpret_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * N * DV;
 
   // constant parts of both buffers: Q' columns 16..31 = (1, 0, ...);
-  // K'^T rows 17..31 = 0.
+  // K'^T row 17 = 0.
   for (int i = tid; i < 2 * C * 16; i += NTHR) {
     const int b = i / (C * 16), rest = i % (C * 16), row = rest / 16, col = 16 + rest % 16;
     sm.qp(b)[row * QP_P + col] = static_cast<__bf16>(col == 16 ? 1.f : 0.f);
   }
-  for (int i = tid; i < 2 * 15 * KT_P; i += NTHR) {
-    const int b = i / (15 * KT_P), rest = i % (15 * KT_P);
-    sm.kt(b)[17 * KT_P + rest] = static_cast<__bf16>(0.f);
-  }
+  for (int i = tid; i < 2 * KF_P; i += NTHR) sm.kt(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
   __syncthreads();
 
   // ---------------------------------------------------------------- roles
@@ -413,15 +443,16 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       const int row = l >> 1, half = l & 1;
       *reinterpret_cast<uint4*>(sm.kr(b) + row * K_P + 8 * half) = pk[SL];
       const bf16x8 e = __builtin_bit_cast(bf16x8, pk[SL]);
-      __bf16* kt = sm.kt(b);
+      const f16x8 eh = to_h8(e);
+      _Float16* kt = sm.kt(b);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kt[(8 * half + u) * KT_P + row] = e[u];
-      if (half == 0) kt[16 * KT_P + row] = static_cast<__bf16>(t0 + c * C + row < t1 ? 1.f : 0.f);
-      __bf16* vt = sm.vt(b);
+      for (int u = 0; u < 8; ++u) kt[(8 * half + u) * KF_P + row] = eh[u];
+      if (half == 0) kt[16 * KF_P + row] = static_cast<_Float16>(t0 + c * C + row < t1 ? 1.f : 0.f);
+      _Float16* vt = sm.vt(b);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int vrow = 8 * k + (l & 7), c8 = l >> 3;
-        const bf16x8 ev = __builtin_bit_cast(bf16x8, pv[SL][k]);
+        const f16x8 ev = to_h8(__builtin_bit_cast(bf16x8, pv[SL][k]));
 #pragma unroll
         for (int u = 0; u < 8; ++u) vt[(8 * c8 + u) * VT_P + vrow] = ev[u];
       }
@@ -429,17 +460,14 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) pv[SL][k] = load_v(c + PD, k);
     }
-    const __bf16* kt = sm.kt(b);
+    const _Float16* kt = sm.kt(b);
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 x = ld8(kt + fk_i[ft] * KT_P + 16 * u + 8 * lh);
-        const bf16x8 y = ld8(kt + fk_j[ft] * KT_P + 16 * u + 8 * lh);
-        bf16x8 out;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) out[s] = static_cast<__bf16>(static_cast<float>(x[s]) * static_cast<float>(y[s]));
-        st8(sm.fk(b) + (32 * ft + lc) * FK_P + 16 * u + 8 * lh, out);
+        const f16x8 x = ldh8(kt + fk_i[ft] * KF_P + 16 * u + 8 * lh);
+        const f16x8 y = ldh8(kt + fk_j[ft] * KF_P + 16 * u + 8 * lh);
+        *reinterpret_cast<f16x8*>(sm.fk(b) + (32 * ft + lc) * FK_P + 16 * u + 8 * lh) = x * y;
       }
     }
   };
@@ -448,8 +476,9 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   auto z_update = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const bf16x8 x = ld8(sm.kt(b) + lc * KT_P + 16 * u + 8 * lh);
-      Z = mfma32(x, x, Z);
+      // rows 18..31 of K' are zero
+      const f16x8 x = ldh8(sm.kt(b) + (lc < 18 ? lc : 17) * KF_P + 16 * u + 8 * lh);
+      Z = mfma32h(x, x, Z);
     }
   };
 
@@ -522,16 +551,17 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
         const bf16x8 kf = ld8(sm.kr(b) + lc * K_P + 8 * lh);
         const bf16x8 qf = ld8(sm.qp(b) + lc * QP_P + 8 * lh);
         const f32x16 sc = mfma32(kf, qf, f32x16{});
-        bf16x8 P0, P1;
+        f16x8 P0, P1;
         float den = 0.f;
+        const float c2 = 0.5f * inv_a * inv_a;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = acc_row(j, lh);
-          const float x = sc[j] * inv_a;
-          float wv = __builtin_fmaf(__builtin_fmaf(0.5f, x, 1.f), x, 1.f);
+          // 1 + y/a + y^2/(2a^2) for the raw score y = q.k
+          float wv = __builtin_fmaf(__builtin_fmaf(c2, sc[j], inv_a), sc[j], 1.f);
           if (key > lc) wv = 0.f;  // causal mask (key after query)
-          const __bf16 pb = static_cast<__bf16>(wv);
-          den += static_cast<float>(pb);
+          const _Float16 pb = static_cast<_Float16>(wv);
+          den += wv;
           if (j < 8)
             P0[j] = pb;
           else
@@ -549,9 +579,9 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
           O = mfma32(sa, ld8(fq + 16 * K), O);
         }
         // intra-chunk term: O^T += V^T P^T, keys in the accumulator order
-        const __bf16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
-        O = mfma32(cat44(ld4(vrow + 4 * lh), ld4(vrow + 8 + 4 * lh)), P0, O);
-        O = mfma32(cat44(ld4(vrow + 16 + 4 * lh), ld4(vrow + 24 + 4 * lh)), P1, O);
+        const _Float16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
+        O = mfma32h(cath44(ldh4(vrow + 4 * lh), ldh4(vrow + 8 + 4 * lh)), P0, O);
+        O = mfma32h(cath44(ldh4(vrow + 16 + 4 * lh), ldh4(vrow + 24 + 4 * lh)), P1, O);
         den += __shfl_xor(den, 32);
         den += sm.den(b)[lc];
         const float rd = 1.f / den;
@@ -592,13 +622,13 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
         }
       }
       if (update) {
-        const __bf16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
+        const _Float16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const bf16x8 bv = ld8(vrow + 16 * u + 8 * lh);
+          const f16x8 bv = ldh8(vrow + 16 * u + 8 * lh);
 #pragma unroll
           for (int ft = 0; ft < NFT; ++ft)
-            S[ft] = mfma32(ld8(sm.fk(b) + (32 * ft + lc) * FK_P + 16 * u + 8 * lh), bv, S[ft]);
+            S[ft] = mfma32h(ldh8(sm.fk(b) + (32 * ft + lc) * FK_P + 16 * u + 8 * lh), bv, S[ft]);
         }
       }
     }
@@ -697,6 +727,153 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   }
 }
 
+// Per-segment state sums (segments 0..P-2), update only: S += phi(K)^T V and
+// Z += K'^T K' over the segment. Five symmetric waves; wave w owns feature
+// tile w (32 features) for all 64 value columns and builds its own phi(K)^T
+// fragments from an fp32 K'^T in LDS, so the work per wave is a handful of
+// fragments and MFMAs per chunk and the pass runs at the speed of streaming
+// K and V. Chunks of 64 tokens, two LDS buffers, loads two chunks ahead.
+namespace ss {
+constexpr int C = 64;
+constexpr int NW = NFT;                   // one wave per 32-feature tile
+constexpr int NTHR = NW * 64;
+constexpr int KF_P = 72;                  // fp16 K'^T rows 0..17, 64 keys + pad
+constexpr int VT_P = 72;                  // fp16 V^T rows, 64 keys + pad
+constexpr int OFF_KF = 0;
+constexpr int OFF_VT = 18 * KF_P * 2;
+constexpr int BUF = OFF_VT + DV * VT_P * 2;
+constexpr int KITEMS = C * D / 8;         // 16-byte items of K per chunk
+constexpr int ITEMS = KITEMS + C * DV / 8;
+constexpr int PER_T = ITEMS / NTHR;       // items per thread
+static_assert(ITEMS % NTHR == 0, "whole items per thread");
+static_assert(KITEMS % 64 == 0, "K items fill whole waves");
+static_assert(OFF_VT % 16 == 0 && BUF % 16 == 0 && (KF_P * 2) % 16 == 0 && (VT_P * 2) % 16 == 0,
+              "16-byte aligned rows");
+}  // namespace ss
+
+__global__ __launch_bounds__(ss::NTHR) void o2_segsum(PrefillArgs a) {
+  constexpr int C = ss::C, NTHR = ss::NTHR, KF_P = ss::KF_P, VT_P = ss::VT_P, BUF = ss::BUF;
+  constexpr int OFF_KF = ss::OFF_KF, OFF_VT = ss::OFF_VT, KITEMS = ss::KITEMS, PER_T = ss::PER_T;
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lc = l & 31, lh = l >> 5;
+  const int PS = a.P - 1;
+  const int unit = blockIdx.x;
+  if (unit >= a.BH * PS) return;
+  const int bh = unit / PS;
+  const int p = unit - bh * PS;
+  const int N = a.N;
+  const int t0 = p * a.L;
+  const int t1 = min(N, t0 + a.L);
+  const int nch = (t1 - t0 + C - 1) / C;
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(a.k) + (static_cast<size_t>(bh) * N + t0) * D,
+                            seg_rows * D * 2);
+  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(a.v) + (static_cast<size_t>(bh) * N + t0) * DV,
+                            seg_rows * DV * 2);
+  auto kf = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_KF); };
+  auto vt = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_VT); };
+  for (int i = tid; i < 2 * KF_P; i += NTHR) kf(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
+
+  auto crow = [&](int c, int row) __attribute__((always_inline)) -> uint32_t {
+    const int r = c * C + row;
+    return static_cast<uint32_t>(r < static_cast<int>(seg_rows) ? r : static_cast<int>(seg_rows));
+  };
+  // Item e of a chunk: K rows (two 16-byte items per key) first, then V rows
+  // (eight per key). Thread tid holds items tid + k*NTHR; the K items are
+  // exactly slot 0 of the first KITEMS/64 waves, so the choice between the
+  // two buffers is uniform per wave.
+  auto is_k = [&](int k) __attribute__((always_inline)) { return k == 0 && w < KITEMS / 64; };
+  auto load_item = [&](int c, int k) __attribute__((always_inline)) -> uint4 {
+    const int e = tid + k * NTHR;
+    if (is_k(k)) return bload16(rk, (crow(c, e >> 1) * D + 8 * (e & 1)) * 2);
+    const int j = e - KITEMS;
+    return bload16(rv, (crow(c, j >> 3) * DV + 8 * (j & 7)) * 2);
+  };
+  auto store_item = [&](int c, int b, int k, uint4 x) __attribute__((always_inline)) {
+    const int e = tid + k * NTHR;
+    const f16x8 v = to_h8(__builtin_bit_cast(bf16x8, x));
+    if (is_k(k)) {
+      const int row = e >> 1, half = e & 1;
+      _Float16* kk = kf(b);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kk[(8 * half + u) * KF_P + row] = v[u];
+      if (half == 0) kk[16 * KF_P + row] = static_cast<_Float16>(c * C + row < static_cast<int>(seg_rows) ? 1.f : 0.f);
+    } else {
+      const int j = e - KITEMS, row = j >> 3, c8 = j & 7;
+      _Float16* t = vt(b);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[(8 * c8 + u) * VT_P + row] = v[u];
+    }
+  };
+
+  uint4 pf[2][PER_T];
+  auto stage = [&](int c, int b, auto slot) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      store_item(c, b, k, pf[SL][k]);
+      pf[SL][k] = load_item(c + 2, k);
+    }
+  };
+
+  const Feat fe = feat(32 * w + lc);
+  f32x16 S0 = f32x16{}, S1 = f32x16{}, Z = f32x16{};
+  auto compute = [&](int b) __attribute__((always_inline)) {
+    const _Float16* k = kf(b);
+    const _Float16* v = vt(b);
+#pragma unroll
+    for (int u = 0; u < C / 16; ++u) {
+      const f16x8 af = ldh8(k + fe.i * KF_P + 16 * u + 8 * lh) * ldh8(k + fe.j * KF_P + 16 * u + 8 * lh);
+      S0 = mfma32h(af, ldh8(v + lc * VT_P + 16 * u + 8 * lh), S0);
+      S1 = mfma32h(af, ldh8(v + (32 + lc) * VT_P + 16 * u + 8 * lh), S1);
+      if (w == 0) {
+        // rows 18..31 of K' are zero
+        const f16x8 zf = ldh8(k + (lc < 18 ? lc : 17) * KF_P + 16 * u + 8 * lh);
+        Z = mfma32h(zf, zf, Z);
+      }
+    }
+  };
+
+  using S0_ = std::integral_constant<int, 0>;
+  using S1_ = std::integral_constant<int, 1>;
+#pragma unroll
+  for (int k = 0; k < PER_T; ++k) {
+    pf[0][k] = load_item(0, k);
+    pf[1][k] = load_item(1, k);
+  }
+  stage(0, 0, S0_{});
+  __syncthreads();
+  int i = 0;
+  for (; i + 2 <= nch; i += 2) {
+    stage(i + 1, 1, S1_{});
+    compute(0);
+    __syncthreads();
+    stage(i + 2, 0, S0_{});
+    compute(1);
+    __syncthreads();
+  }
+  if (i < nch) {
+    stage(i + 1, 1, S1_{});
+    compute(0);
+    __syncthreads();
+  }
+
+  // sums in the accumulator layout of the main kernel's state waves
+  float4* dst = reinterpret_cast<float4*>(a.seg) + (static_cast<size_t>(bh) * PS + p) * UNIT_F4;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    dst[((0 * NFT + w) * 4 + q4) * 64 + l] = float4{S0[4 * q4], S0[4 * q4 + 1], S0[4 * q4 + 2], S0[4 * q4 + 3]};
+    dst[((1 * NFT + w) * 4 + q4) * 64 + l] = float4{S1[4 * q4], S1[4 * q4 + 1], S1[4 * q4 + 2], S1[4 * q4 + 3]};
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      dst[(2 * NFT * 4 + q4) * 64 + l] = float4{Z[4 * q4], Z[4 * q4 + 1], Z[4 * q4 + 2], Z[4 * q4 + 3]};
+  }
+}
+
 // Inclusive prefix over the segments of each head, in place.
 __global__ __launch_bounds__(256) void o2_scan(float4* seg, int BH, int PS) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -790,7 +967,7 @@ bool plan(int BH, int N, PrefillPlan* pl) {
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   hipError_t e;
   if (a.P > 1) {
-    hipLaunchKernelGGL((o2_kernel<SEGSUM, true>), dim3(a.BH * (a.P - 1)), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL(o2_segsum, dim3(a.BH * (a.P - 1)), dim3(ss::NTHR), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.P > 2) {
       const int64_t n = static_cast<int64_t>(a.BH) * UNIT_F4;
