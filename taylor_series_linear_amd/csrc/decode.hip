@@ -34,10 +34,12 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
 template <int D, int DV, int NT, bool BF16>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int F = feature_count(D, NT);
-  constexpr int NQ = DV / 4;         // float4 columns per state row
-  constexpr int NG = 256 / NQ;       // row groups
+  constexpr int NQ = DV / 4;              // float4 columns per state row
+  constexpr int NG = 256 / NQ;            // row groups
   constexpr int RPT = (F + NG - 1) / NG;  // rows per thread (upper bound)
-  constexpr int BATCH = RPT < 8 ? RPT : 8;
+  // rows whose loads are in flight at once; the whole share when it is small
+  constexpr int BATCH = RPT <= 12 ? RPT : 8;
+  constexpr int ZPT = (F + 255) / 256;    // z entries per thread
 
   __shared__ float sq[D], sk[D];
   __shared__ __attribute__((aligned(16))) float sv[DV];
@@ -48,6 +50,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const float inv_a = a.inv_a;
+  const int dq = tid % NQ;
+  const int rg = tid / NQ;
+  float* Sh = a.S + static_cast<size_t>(bh) * F * DV;
+  float* zh = a.z + static_cast<size_t>(bh) * F;
+
+  // The state rows do not depend on q, k or v: their loads go out first, so
+  // the state read overlaps the small input loads and the feature map.
+  f32x4 rows[BATCH];
+  auto load_batch = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int f = rg + NG * (r0 + j);
+      if (r0 + j < RPT && f < F) rows[j] = *reinterpret_cast<const f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq);
+    }
+  };
+  load_batch(0);
+  float zv[ZPT];
+#pragma unroll
+  for (int j = 0; j < ZPT; ++j) {
+    const int f = tid + 256 * j;
+    zv[j] = f < F ? zh[f] : 0.f;
+  }
 
   if (tid < D) {
     sq[tid] = load_in<BF16>(a.q, static_cast<size_t>(bh) * D + tid);
@@ -71,18 +95,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  const int dq = tid % NQ;
-  const int rg = tid / NQ;
-  float* Sh = a.S + static_cast<size_t>(bh) * F * DV;
   const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * dq);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int r0 = 0; r0 < RPT; r0 += BATCH) {
-    f32x4 rows[BATCH];
-#pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int f = rg + NG * (r0 + j);
-      if (r0 + j < RPT && f < F) rows[j] = *reinterpret_cast<const f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq);
-    }
+    if (r0 > 0) load_batch(r0);
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int f = rg + NG * (r0 + j);
@@ -94,11 +110,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
   }
   float dpart = 0.f;
-  float* zh = a.z + static_cast<size_t>(bh) * F;
-  for (int f = tid; f < F; f += 256) {
-    const float zz = zh[f] + sfk[f];
-    zh[f] = zz;
-    dpart += sfq[f] * zz;
+#pragma unroll
+  for (int j = 0; j < ZPT; ++j) {
+    const int f = tid + 256 * j;
+    if (f < F) {
+      const float zz = zv[j] + sfk[f];
+      zh[f] = zz;
+      dpart += sfq[f] * zz;
+    }
   }
   red[tid] = acc;
   dred[tid] = dpart;
