@@ -14,6 +14,7 @@ struct PrefillPlan {
   size_t seg_off = 0;    // byte offsets into the workspace
   size_t fin_off = 0;
   size_t part_off = 0;
+  size_t sync_off = 0;   // flags and tickets of single-pass kernels
   size_t bytes = 0;      // workspace size
 };
 
@@ -30,6 +31,7 @@ struct PrefillArgs {
   float* seg;   // per-segment state sums (layout private to the kernel family)
   float* fin;   // final-state staging for in-place continuation (defer_state)
   float* part;  // partial outputs of feature-sliced kernels
+  int* sync;    // flags and work tickets of single-pass kernels (cleared by the launch)
   int BH;
   int N;
   int P;        // segments per head

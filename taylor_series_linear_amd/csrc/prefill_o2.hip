@@ -107,6 +107,20 @@ static_assert(OFF_K % 16 == 0 && OFF_KT % 16 == 0 && (KF_P * 2) % 16 == 0 && OFF
 constexpr int UNIT_F4 = 2 * NFT * 4 * 64 + 4 * 64;   // float4 count
 constexpr size_t UNIT_BYTES = static_cast<size_t>(UNIT_F4) * 16;
 
+// Segment-sum pass (phase 1 of the kernel below): chunks of 128 tokens staged
+// by all four waves into its own LDS layout (K'^T rows 0..17 and V^T rows,
+// fp16, 272-byte rows so consecutive rows start 4 banks apart).
+namespace s1 {
+constexpr int C = 128;
+constexpr int P = C + 8;                 // row pitch in halves
+constexpr int KROWS = 18;
+constexpr int BUF = (KROWS + DV) * P * 2;
+constexpr int NV = C * DV / 8 / NTHR;    // 16-byte V items per thread (K: one)
+static_assert(C * D / 8 == NTHR && (C * DV / 8) % NTHR == 0, "whole items per thread");
+static_assert(2 * BUF <= lds_bytes<true>() && 2 * BUF <= lds_bytes<false>(), "fits the kernel's LDS");
+static_assert(BUF % 16 == 0 && (P * 2) % 16 == 0, "16-byte aligned rows");
+}  // namespace s1
+
 // ---------------------------------------------------------------------------
 // internal feature basis
 // ---------------------------------------------------------------------------
@@ -202,6 +216,10 @@ __device__ __forceinline__ f32x8 ldf8(const float* p) {
 }
 __device__ __forceinline__ void st8(__bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// cache-policy operand of buffer accesses: device scope (sc1)
+constexpr int kDeviceScope = 16;
+
 // Raw buffer resource over `bytes` bytes at p (gfx9 descriptor word 3);
 // loads outside the range return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -240,11 +258,18 @@ struct Smem {
 // the kernel
 // ---------------------------------------------------------------------------
 
-enum { SEGSUM = 0, MAIN = 1 };
+// Sync area of the single-pass launch (ints): one flag per (head, segment),
+// then the work-ticket counter. o2_reset clears it at the start of a call.
+__host__ __device__ constexpr int sync_ints(int units) { return units + 64; }
 
-template <int MODE, bool OBF>
+__global__ __launch_bounds__(256) void o2_reset(int* sync, int n) {
+  for (int i = threadIdx.x; i < n; i += 256) sync[i] = 0;
+}
+
+template <bool OBF>
 __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem_raw[lds_bytes<OBF>()];
+  __shared__ int s_unit;
   const Smem sm{smem_raw};
   constexpr int OP = OStage<OBF>::P;
   constexpr int OB = OStage<OBF>::BYTES;
@@ -259,14 +284,23 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   const int lc = l & 31;
   const int lh = l >> 5;
 
-  const int PL = MODE == MAIN ? a.P : a.P - 1;
-  const int unit = blockIdx.x;
-  if (unit >= a.BH * PL) return;
-  const int bh = unit / PL;
-  const int p = unit - bh * PL;
-  const bool want_out = MODE == MAIN && a.o != nullptr;
-  const bool want_state = MODE == MAIN && a.S != nullptr && p == a.P - 1;
-  if (MODE == MAIN && !want_out && !want_state) return;
+  const int P = a.P;
+  const int units = a.BH * P;
+  int* const flags = a.sync;
+  // Work unit. With several segments the unit comes from a ticket counter,
+  // so tickets follow dispatch order: a workgroup only ever waits for
+  // segments of lower tickets, whose workgroups are already running and
+  // publish their sums without waiting themselves.
+  if (tid == 0) s_unit = P > 1 ? atomicAdd(flags + units, 1) : static_cast<int>(blockIdx.x);
+  __syncthreads();
+  const int unit = __builtin_amdgcn_readfirstlane(s_unit);
+  if (unit >= units) return;
+  const int bh = unit / P;
+  const int p = unit - bh * P;
+  const bool want_out = a.o != nullptr;
+  const bool want_state = a.S != nullptr && p == P - 1;
+  const bool publish = p < P - 1;  // later segments of the head read this one's sum
+  if (!want_out && !want_state && !publish) return;
   const int N = a.N;
   const int t0 = p * a.L;
   const int t1 = min(N, t0 + a.L);
@@ -277,15 +311,6 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   const __bf16* kh = reinterpret_cast<const __bf16*>(a.k) + static_cast<size_t>(bh) * N * D;
   const __bf16* vh = reinterpret_cast<const __bf16*>(a.v) + static_cast<size_t>(bh) * N * DV;
 
-  // constant parts of both buffers: Q' columns 16..31 = (1, 0, ...);
-  // K'^T row 17 = 0.
-  for (int i = tid; i < 2 * C * 16; i += NTHR) {
-    const int b = i / (C * 16), rest = i % (C * 16), row = rest / 16, col = 16 + rest % 16;
-    sm.qp(b)[row * QP_P + col] = static_cast<__bf16>(col == 16 ? 1.f : 0.f);
-  }
-  for (int i = tid; i < 2 * KF_P; i += NTHR) sm.kt(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
-  __syncthreads();
-
   // ---------------------------------------------------------------- roles
   // M waves: state S[ft] (rows 32 ft + acc_row, column 32 w + lc).
   f32x16 S[NFT];
@@ -295,74 +320,6 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   uint4 pq[PD];
   uint4 pk[PD];
   uint4 pv[PD][4];
-
-  const float4* segp = reinterpret_cast<const float4*>(a.seg);
-
-  // initial state ----------------------------------------------------------
-  if (w < 2) {
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) S[ft] = f32x16{};
-    if (MODE == MAIN) {
-      if (p > 0) {
-        const float4* src = segp + (static_cast<size_t>(bh) * (a.P - 1) + (p - 1)) * UNIT_F4 +
-                            (static_cast<size_t>(w) * NFT) * 4 * 64 + l;
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 x = src[(ft * 4 + q4) * 64];
-            S[ft][4 * q4 + 0] = x.x;
-            S[ft][4 * q4 + 1] = x.y;
-            S[ft][4 * q4 + 2] = x.z;
-            S[ft][4 * q4 + 3] = x.w;
-          }
-      }
-      if (a.S0 != nullptr) {
-        const int col = 32 * w + lc;
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const Feat e = feat(32 * ft + acc_row(j, lh));
-            if (e.can >= 0)
-              S[ft][j] += a.S0[(static_cast<size_t>(bh) * 153 + e.can) * DV + col] / e.wcan;
-          }
-      }
-    }
-  } else if (w == 2) {
-    Z = f32x16{};
-    if (MODE == MAIN) {
-      if (p > 0) {
-        const float4* src = segp + (static_cast<size_t>(bh) * (a.P - 1) + (p - 1)) * UNIT_F4 +
-                            2 * NFT * 4 * 64 + l;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 x = src[q4 * 64];
-          Z[4 * q4 + 0] = x.x;
-          Z[4 * q4 + 1] = x.y;
-          Z[4 * q4 + 2] = x.z;
-          Z[4 * q4 + 3] = x.w;
-        }
-      }
-      if (a.z0 != nullptr) {
-        const float* z0 = a.z0 + static_cast<size_t>(bh) * 153;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = acc_row(j, lh), c = lc;
-          float x = 0.f;
-          if (r < 16 && c < 16) {
-            const int lo = r < c ? r : c, hi = r < c ? c : r;
-            x = z0[17 + lo * 16 - lo * (lo - 1) / 2 + (hi - lo)] / (r == c ? 1.f : kSqrt2);
-          } else if ((r < 16 && c == 16) || (r == 16 && c < 16)) {
-            x = z0[1 + (r < c ? r : c)];
-          } else if (r == 16 && c == 16) {
-            x = z0[0];
-          }
-          Z[j] += x;
-        }
-      }
-    }
-  }
 
   // staging helpers ---------------------------------------------------------
   // Loads go through buffer resources bounded by the segment: rows past its
@@ -512,389 +469,414 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
     if (lh == 0) sm.den(b)[lc] = part;
   };
 
-  // prologue: fill the prefetch ring and prepare chunk 0 ------------------
-  static_assert(PD == 2, "the chunk loop below is unrolled for two ring slots");
+  // M wave: one chunk from buffer b. OUT: read out and store the chunk's
+  // outputs; UPD: fold the chunk into S.
+  auto m_chunk = [&](int i, bool out, bool upd) __attribute__((always_inline)) {
+    const int b = i & 1;
+    const int m = w;
+    if (out) {
+      // score tile D[key][query] = K Q^T (both raw), weights and mask
+      const bf16x8 kf = ld8(sm.kr(b) + lc * K_P + 8 * lh);
+      const bf16x8 qf = ld8(sm.qp(b) + lc * QP_P + 8 * lh);
+      const f32x16 sc = mfma32(kf, qf, f32x16{});
+      f16x8 P0, P1;
+      float den = 0.f;
+      const float c2 = 0.5f * inv_a * inv_a;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = acc_row(j, lh);
+        // 1 + y/a + y^2/(2a^2) for the raw score y = q.k
+        float wv = __builtin_fmaf(__builtin_fmaf(c2, sc[j], inv_a), sc[j], 1.f);
+        if (key > lc) wv = 0.f;  // causal mask (key after query)
+        const _Float16 pb = static_cast<_Float16>(wv);
+        den += wv;
+        if (j < 8)
+          P0[j] = pb;
+        else
+          P1[j - 8] = pb;
+      }
+      // read-out: O^T[dv][query] = S^T phi~(Q)^T over 10 k-steps
+      f32x16 O = f32x16{};
+      const __bf16* fq = sm.fq(b) + lc * FQ_P + 8 * lh;
+#pragma unroll
+      for (int K = 0; K < 10; ++K) {
+        const int ft = K >> 1, u = K & 1;
+        bf16x8 sa;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sa[s] = static_cast<__bf16>(S[ft][8 * u + s]);
+        O = mfma32(sa, ld8(fq + 16 * K), O);
+      }
+      // intra-chunk term: O^T += V^T P^T, keys in the accumulator order
+      const _Float16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
+      O = mfma32h(cath44(ldh4(vrow + 4 * lh), ldh4(vrow + 8 + 4 * lh)), P0, O);
+      O = mfma32h(cath44(ldh4(vrow + 16 + 4 * lh), ldh4(vrow + 24 + 4 * lh)), P1, O);
+      den += __shfl_xor(den, 32);
+      den += sm.den(b)[lc];
+      const float rd = 1.f / den;
+      // normalise, transpose through this wave's LDS area, store rows
+      char* st = sm.ostage(m, OB);
+      const int rows = min(C, t1 - (t0 + i * C));
+      const size_t orow0 = static_cast<size_t>(bh) * N + t0 + i * C;
+      if constexpr (OBF) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          bf16x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(O[4 * bb + r] * rd);
+          *reinterpret_cast<bf16x4*>(st + (lc * OP + 8 * bb + 4 * lh) * 2) = ov;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int e = l + 64 * k, row = e >> 2, c4 = e & 3;
+          const uint4 x = *reinterpret_cast<const uint4*>(st + (row * OP + 8 * c4) * 2);
+          if (row < rows)
+            *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.o) + (orow0 + row) * DV + 32 * m + 8 * c4) = x;
+        }
+      } else {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          f32x4 ov;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = O[4 * bb + r] * rd;
+          *reinterpret_cast<f32x4*>(st + (lc * OP + 8 * bb + 4 * lh) * 4) = ov;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = l + 64 * k, row = e >> 3, c8 = e & 7;
+          const uint4 x = *reinterpret_cast<const uint4*>(st + (row * OP + 4 * c8) * 4);
+          if (row < rows)
+            *reinterpret_cast<uint4*>(reinterpret_cast<float*>(a.o) + (orow0 + row) * DV + 32 * m + 4 * c8) = x;
+        }
+      }
+    }
+    if (upd) {
+      const _Float16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f16x8 bv = ldh8(vrow + 16 * u + 8 * lh);
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+          S[ft] = mfma32h(ldh8(sm.fk(b) + (32 * ft + lc) * FK_P + 16 * u + 8 * lh), bv, S[ft]);
+      }
+    }
+  };
+
+  // One pass over the segment's chunks. Chunk i is consumed by the M waves
+  // from buffer i&1 while the Q and K waves prepare chunk i+1 in the other
+  // buffer; one barrier per chunk. Each role runs its own loop so the
+  // compiler's wait counts see only that role's memory operations. OUT
+  // selects the output pass (read-out, outputs, Q staging); without it the
+  // pass only sums the segment's state (S and Z).
+  static_assert(PD == 2, "the chunk loops below are unrolled for two ring slots");
   using S0_ = std::integral_constant<int, 0>;
   using S1_ = std::integral_constant<int, 1>;
-  if (w == 2 && want_out) {
-    pq[0] = load_q(0);
-    pq[1] = load_q(1);
-    produce_q(0, 0, S0_{});
-  }
-  if (w == 3) {
-    pk[0] = load_k(0);
-    pk[1] = load_k(1);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      pv[0][k] = load_v(0, k);
-      pv[1][k] = load_v(1, k);
+  auto pass = [&](auto out_tag) __attribute__((always_inline)) {
+    constexpr bool OUT = decltype(out_tag)::value;
+    const bool qout = OUT && want_out;
+    // prologue: fill the prefetch rings and prepare chunk 0
+    if (w == 2 && qout) {
+      pq[0] = load_q(0);
+      pq[1] = load_q(1);
+      produce_q(0, 0, S0_{});
     }
-    produce_k(0, 0, S0_{});
-  }
-  __syncthreads();
-  if (w == 2 && want_out) den_inter(0);
-  __syncthreads();
-
-  // chunk loop ---------------------------------------------------------------
-  // Iteration i: the M waves consume chunk i from buffer i&1 while the Q and
-  // K waves prepare chunk i+1 (ring slot (i+1)&1) in the other buffer.
-  // Each role runs its own loop (one barrier per chunk in each), so the
-  // compiler's wait counts see only that role's memory operations.
-  auto m_iteration = [&](int i) __attribute__((always_inline)) {
-    const int b = i & 1;
-    const bool last = i + 1 == nch;
-    {
-      const int m = w;
-      const bool update = MODE == SEGSUM || !last || want_state;
-      if (want_out) {
-        // score tile D[key][query] = K Q^T (both raw), weights and mask
-        const bf16x8 kf = ld8(sm.kr(b) + lc * K_P + 8 * lh);
-        const bf16x8 qf = ld8(sm.qp(b) + lc * QP_P + 8 * lh);
-        const f32x16 sc = mfma32(kf, qf, f32x16{});
-        f16x8 P0, P1;
-        float den = 0.f;
-        const float c2 = 0.5f * inv_a * inv_a;
+    if (w == 3) {
+      pk[0] = load_k(0);
+      pk[1] = load_k(1);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = acc_row(j, lh);
-          // 1 + y/a + y^2/(2a^2) for the raw score y = q.k
-          float wv = __builtin_fmaf(__builtin_fmaf(c2, sc[j], inv_a), sc[j], 1.f);
-          if (key > lc) wv = 0.f;  // causal mask (key after query)
-          const _Float16 pb = static_cast<_Float16>(wv);
-          den += wv;
-          if (j < 8)
-            P0[j] = pb;
-          else
-            P1[j - 8] = pb;
+      for (int k = 0; k < 4; ++k) {
+        pv[0][k] = load_v(0, k);
+        pv[1][k] = load_v(1, k);
+      }
+      produce_k(0, 0, S0_{});
+    }
+    __syncthreads();
+    if (w == 2 && qout) den_inter(0);
+    __syncthreads();
+    // On its last iteration each staging loop loads and builds an empty
+    // chunk into the idle buffer, which keeps its loads per iteration fixed.
+    if (w < 2) {
+      for (int i = 0; i < nch; ++i) {
+        const bool last = i + 1 == nch;
+        m_chunk(i, qout, !OUT || !last || want_state);
+        __syncthreads();
+      }
+    } else if (w == 2) {
+      if (qout) {
+        auto q_it = [&](int i, auto slot) __attribute__((always_inline)) {
+          const int b = i & 1, nb = b ^ 1;
+          produce_q(i + 1, nb, slot);
+          z_update(b);
+          den_inter(nb);
+        };
+        int i = 0;
+        for (; i + 2 <= nch; i += 2) {
+          q_it(i, S1_{});
+          __syncthreads();
+          q_it(i + 1, S0_{});
+          __syncthreads();
         }
-        // read-out: O^T[dv][query] = S^T phi~(Q)^T over 10 k-steps
-        f32x16 O = f32x16{};
-        const __bf16* fq = sm.fq(b) + lc * FQ_P + 8 * lh;
-#pragma unroll
-        for (int K = 0; K < 10; ++K) {
-          const int ft = K >> 1, u = K & 1;
-          bf16x8 sa;
-#pragma unroll
-          for (int s = 0; s < 8; ++s) sa[s] = static_cast<__bf16>(S[ft][8 * u + s]);
-          O = mfma32(sa, ld8(fq + 16 * K), O);
+        if (i < nch) {
+          q_it(i, S1_{});
+          __syncthreads();
         }
-        // intra-chunk term: O^T += V^T P^T, keys in the accumulator order
-        const _Float16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
-        O = mfma32h(cath44(ldh4(vrow + 4 * lh), ldh4(vrow + 8 + 4 * lh)), P0, O);
-        O = mfma32h(cath44(ldh4(vrow + 16 + 4 * lh), ldh4(vrow + 24 + 4 * lh)), P1, O);
-        den += __shfl_xor(den, 32);
-        den += sm.den(b)[lc];
-        const float rd = 1.f / den;
-        // normalise, transpose through this wave's LDS area, store rows
-        char* st = sm.ostage(m, OB);
-        const int rows = min(C, t1 - (t0 + i * C));
-        const size_t orow0 = static_cast<size_t>(bh) * N + t0 + i * C;
-        if constexpr (OBF) {
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            bf16x4 ov;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ov[r] = static_cast<__bf16>(O[4 * bb + r] * rd);
-            *reinterpret_cast<bf16x4*>(st + (lc * OP + 8 * bb + 4 * lh) * 2) = ov;
-          }
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int e = l + 64 * k, row = e >> 2, c4 = e & 3;
-            const uint4 x = *reinterpret_cast<const uint4*>(st + (row * OP + 8 * c4) * 2);
-            if (row < rows)
-              *reinterpret_cast<uint4*>(reinterpret_cast<__bf16*>(a.o) + (orow0 + row) * DV + 32 * m + 8 * c4) = x;
-          }
-        } else {
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            f32x4 ov;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ov[r] = O[4 * bb + r] * rd;
-            *reinterpret_cast<f32x4*>(st + (lc * OP + 8 * bb + 4 * lh) * 4) = ov;
-          }
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int e = l + 64 * k, row = e >> 3, c8 = e & 7;
-            const uint4 x = *reinterpret_cast<const uint4*>(st + (row * OP + 4 * c8) * 4);
-            if (row < rows)
-              *reinterpret_cast<uint4*>(reinterpret_cast<float*>(a.o) + (orow0 + row) * DV + 32 * m + 4 * c8) = x;
-          }
+      } else {
+        for (int i = 0; i < nch; ++i) {
+          z_update(i & 1);
+          __syncthreads();
         }
       }
-      if (update) {
-        const _Float16* vrow = sm.vt(b) + (32 * m + lc) * VT_P;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const f16x8 bv = ldh8(vrow + 16 * u + 8 * lh);
-#pragma unroll
-          for (int ft = 0; ft < NFT; ++ft)
-            S[ft] = mfma32h(ldh8(sm.fk(b) + (32 * ft + lc) * FK_P + 16 * u + 8 * lh), bv, S[ft]);
-        }
-      }
-    }
-  };
-  // Q and K waves: prepare chunk i+1 (on the last iteration this loads and
-  // builds an empty chunk into the idle buffer, which keeps the number of
-  // loads per iteration constant).
-  auto q_iteration = [&](int i, auto slot) __attribute__((always_inline)) {
-    const int b = i & 1, nb = b ^ 1;
-    produce_q(i + 1, nb, slot);
-    z_update(b);
-    den_inter(nb);
-  };
-  auto k_iteration = [&](int i, auto slot) __attribute__((always_inline)) { produce_k(i + 1, (i & 1) ^ 1, slot); };
-  if (w < 2) {
-    for (int i = 0; i < nch; ++i) {
-      m_iteration(i);
-      __syncthreads();
-    }
-  } else if (w == 2) {
-    if (want_out) {
+    } else {
+      auto k_it = [&](int i, auto slot) __attribute__((always_inline)) { produce_k(i + 1, (i & 1) ^ 1, slot); };
       int i = 0;
       for (; i + 2 <= nch; i += 2) {
-        q_iteration(i, S1_{});
+        k_it(i, S1_{});
         __syncthreads();
-        q_iteration(i + 1, S0_{});
+        k_it(i + 1, S0_{});
         __syncthreads();
       }
       if (i < nch) {
-        q_iteration(i, S1_{});
-        __syncthreads();
-      }
-    } else {
-      for (int i = 0; i < nch; ++i) {
-        z_update(i & 1);
+        k_it(i, S1_{});
         __syncthreads();
       }
     }
-  } else {
+  };
+
+  float4* const segu = reinterpret_cast<float4*>(a.seg);
+  auto unit_ptr = [&](int q) __attribute__((always_inline)) {
+    return segu + (static_cast<size_t>(bh) * (P - 1) + q) * UNIT_F4;
+  };
+  // float4 index of (value half h, feature tile ft, register quad q4, lane)
+  auto unit_idx = [&](int h, int ft, int q4) __attribute__((always_inline)) { return ((h * NFT + ft) * 4 + q4) * 64 + l; };
+  constexpr int ZIDX = 2 * NFT * 4 * 64;
+  // Published sums are written and read with device-scope (sc1) buffer
+  // accesses, so the flag needs only the stores' completion before it and
+  // no cache write-back or invalidation around it.
+  auto st_dev = [&](__amdgpu_buffer_rsrc_t r, int idx, const f32x16& x, int q4) __attribute__((always_inline)) {
+    const f32x4 v{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, idx * 16, 0, kDeviceScope);
+  };
+  auto ld_dev = [&](__amdgpu_buffer_rsrc_t r, int idx) __attribute__((always_inline)) -> f32x4 {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, idx * 16, 0, kDeviceScope));
+  };
+
+  // phase 1: this segment's own sum, published for the later segments ------
+  if (publish) {
+    constexpr int C1 = s1::C, P1 = s1::P, NV = s1::NV;
+    auto kt1 = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem_raw + b * s1::BUF); };
+    auto vt1 = [&](int b) __attribute__((always_inline)) {
+      return reinterpret_cast<_Float16*>(smem_raw + b * s1::BUF + s1::KROWS * P1 * 2);
+    };
+    // V^T row r keeps its 8-token groups XOR-swizzled by r's group of eight,
+    // which spreads the transposing 2-byte writes over the banks.
+    auto vpos = [&](int r, int t) __attribute__((always_inline)) { return t ^ (8 * ((r >> 3) & 7)); };
+    for (int i = tid; i < 2 * C1; i += NTHR) kt1(i / C1)[17 * P1 + i % C1] = static_cast<_Float16>(0.f);
+    auto crow1 = [&](int c, int row) __attribute__((always_inline)) -> uint32_t {
+      const int r = c * C1 + row;
+      return static_cast<uint32_t>(r < static_cast<int>(seg_rows) ? r : static_cast<int>(seg_rows));
+    };
+    uint4 r1[2][1 + NV];
+    auto load1 = [&](int c, uint4* dst) __attribute__((always_inline)) {
+      dst[0] = bload16(rk, (crow1(c, tid >> 1) * D + 8 * (tid & 1)) * 2);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int j = tid + NTHR * k;
+        dst[1 + k] = bload16(rv, (crow1(c, j >> 3) * DV + 8 * (j & 7)) * 2);
+      }
+    };
+    auto stage1 = [&](int c, int b, auto slot) __attribute__((always_inline)) {
+      constexpr int SL = decltype(slot)::value;
+      {
+        const int row = tid >> 1, half = tid & 1;
+        const f16x8 e = to_h8(__builtin_bit_cast(bf16x8, r1[SL][0]));
+        _Float16* kt = kt1(b);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kt[(8 * half + u) * P1 + row] = e[u];
+        if (half == 0) kt[16 * P1 + row] = static_cast<_Float16>(c * C1 + row < static_cast<int>(seg_rows) ? 1.f : 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int j = tid + NTHR * k, row = j >> 3, c8 = j & 7;
+        const f16x8 e = to_h8(__builtin_bit_cast(bf16x8, r1[SL][1 + k]));
+        _Float16* vt = vt1(b);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) vt[(8 * c8 + u) * P1 + vpos(8 * c8 + u, row)] = e[u];
+      }
+      load1(c + 2, r1[SL]);
+    };
+    // Accumulators: wave w owns feature tile w for both value halves (A0,
+    // A1); the third one (A2) is tile 4 for value half w on waves 0 and 1,
+    // Z on wave 2 (K'^T row r times the valid-key row, i.e. K' itself), and
+    // unused on wave 3. The rows are chosen per lane so that every wave runs
+    // the same instructions.
+    const int ftw = w;
+    const Feat fw = feat(32 * ftw + lc), f4 = feat(32 * 4 + lc);
+    const int ra = w < 2 ? f4.i : (w == 2 ? (lc < 18 ? lc : 17) : 17);
+    const int rb = w < 2 ? f4.j : (w == 2 ? 16 : 17);
+    // B operand of A2: V^T row 32w + lc (waves 0, 1) or K'^T row ra (wave 2)
+    const int xrow = w < 2 ? 32 * w + lc : ra;
+    const int xoff = w < 2 ? s1::KROWS * P1 + xrow * P1 : xrow * P1;
+    const int xsw = w < 2 ? 8 * ((xrow >> 3) & 7) : 0;
+    f32x16 A0 = f32x16{}, A1 = f32x16{}, A2 = f32x16{};
+    auto compute1 = [&](int b) __attribute__((always_inline)) {
+      const _Float16* kt = kt1(b);
+      const _Float16* vt = vt1(b);
+#pragma unroll
+      for (int u = 0; u < C1 / 16; ++u) {
+        const int tk = 16 * u + 8 * lh;
+        const f16x8 af = ldh8(kt + fw.i * P1 + tk) * ldh8(kt + fw.j * P1 + tk);
+        const f16x8 b0 = ldh8(vt + lc * P1 + vpos(lc, tk));
+        const f16x8 b1 = ldh8(vt + (32 + lc) * P1 + vpos(32 + lc, tk));
+        const f16x8 xa = ldh8(kt + ra * P1 + tk) * ldh8(kt + rb * P1 + tk);
+        const f16x8 xb = ldh8(kt + xoff + (tk ^ xsw));
+        A0 = mfma32h(af, b0, A0);
+        A1 = mfma32h(af, b1, A1);
+        A2 = mfma32h(xa, xb, A2);
+      }
+    };
+    using T0_ = std::integral_constant<int, 0>;
+    using T1_ = std::integral_constant<int, 1>;
+    const int nch1 = (static_cast<int>(seg_rows) + C1 - 1) / C1;
+    load1(0, r1[0]);
+    load1(1, r1[1]);
+    stage1(0, 0, T0_{});
+    __syncthreads();
     int i = 0;
-    for (; i + 2 <= nch; i += 2) {
-      k_iteration(i, S1_{});
+    for (; i + 2 <= nch1; i += 2) {
+      stage1(i + 1, 1, T1_{});
+      compute1(0);
       __syncthreads();
-      k_iteration(i + 1, S0_{});
+      stage1(i + 2, 0, T0_{});
+      compute1(1);
       __syncthreads();
     }
-    if (i < nch) {
-      k_iteration(i, S1_{});
+    if (i < nch1) {
+      stage1(i + 1, 1, T1_{});
+      compute1(0);
       __syncthreads();
+    }
+    const auto ru = make_rsrc(unit_ptr(p), static_cast<uint32_t>(UNIT_BYTES));
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      st_dev(ru, unit_idx(0, ftw, q4), A0, q4);
+      st_dev(ru, unit_idx(1, ftw, q4), A1, q4);
+      if (w < 2) st_dev(ru, unit_idx(w, 4, q4), A2, q4);
+      if (w == 2) st_dev(ru, ZIDX + q4 * 64 + l, A2, q4);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flags + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!want_out) return;
+  }
+
+  // constant parts of both phase-3 buffers: Q' columns 16..31 = (1, 0, ...);
+  // K'^T row 17 = 0.
+  for (int i = tid; i < 2 * C * 16; i += NTHR) {
+    const int b = i / (C * 16), rest = i % (C * 16), row = rest / 16, col = 16 + rest % 16;
+    sm.qp(b)[row * QP_P + col] = static_cast<__bf16>(col == 16 ? 1.f : 0.f);
+  }
+  for (int i = tid; i < 2 * KF_P; i += NTHR) sm.kt(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
+
+  // phase 2: initial state = S0 + the sums of segments 0..p-1 ---------------
+  if (w < 2) {
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) S[ft] = f32x16{};
+  } else if (w == 2) {
+    Z = f32x16{};
+  }
+  if (p > 0 && tid == 0) {
+    // The wait is bounded (about a second) so that a broken invariant shows
+    // as wrong output rather than a workgroup that never ends.
+    int spins = 0;
+    for (int q = 0; q < p; ++q)
+      while (__hip_atomic_load(flags + bh * P + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
+             ++spins < (1 << 24))
+        __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+  for (int q = 0; q < p; ++q) {
+    const auto ru = make_rsrc(unit_ptr(q), static_cast<uint32_t>(UNIT_BYTES));
+    if (w < 2) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 x = ld_dev(ru, unit_idx(w, ft, q4));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) S[ft][4 * q4 + r] += x[r];
+        }
+    } else if (w == 2) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 x = ld_dev(ru, ZIDX + q4 * 64 + l);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Z[4 * q4 + r] += x[r];
+      }
+    }
+  }
+  if (w < 2 && a.S0 != nullptr) {
+    const int col = 32 * w + lc;
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const Feat e = feat(32 * ft + acc_row(j, lh));
+        if (e.can >= 0) S[ft][j] += a.S0[(static_cast<size_t>(bh) * 153 + e.can) * DV + col] / e.wcan;
+      }
+  } else if (w == 2 && a.z0 != nullptr) {
+    const float* z0 = a.z0 + static_cast<size_t>(bh) * 153;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = acc_row(j, lh), c = lc;
+      float x = 0.f;
+      if (r < 16 && c < 16) {
+        const int lo = r < c ? r : c, hi = r < c ? c : r;
+        x = z0[17 + lo * 16 - lo * (lo - 1) / 2 + (hi - lo)] / (r == c ? 1.f : kSqrt2);
+      } else if ((r < 16 && c == 16) || (r == 16 && c < 16)) {
+        x = z0[1 + (r < c ? r : c)];
+      } else if (r == 16 && c == 16) {
+        x = z0[0];
+      }
+      Z[j] += x;
     }
   }
 
-  // results ------------------------------------------------------------------
-  float4* dstu = nullptr;
-  if (MODE == SEGSUM) {
-    dstu = reinterpret_cast<float4*>(a.seg) + (static_cast<size_t>(bh) * (a.P - 1) + p) * UNIT_F4;
-  } else if (want_state && a.defer_state) {
-    dstu = reinterpret_cast<float4*>(a.fin) + static_cast<size_t>(bh) * UNIT_F4;
-  }
-  if (dstu != nullptr) {
+  // phase 3: outputs (and, for the last segment, the final state) -----------
+  pass(std::true_type{});
+
+  if (!want_state) return;
+  if (a.defer_state) {
+    float4* dst = reinterpret_cast<float4*>(a.fin) + static_cast<size_t>(bh) * UNIT_F4;
     if (w < 2) {
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          dstu[((w * NFT + ft) * 4 + q4) * 64 + l] =
-              float4{S[ft][4 * q4], S[ft][4 * q4 + 1], S[ft][4 * q4 + 2], S[ft][4 * q4 + 3]};
+          dst[unit_idx(w, ft, q4)] = float4{S[ft][4 * q4], S[ft][4 * q4 + 1], S[ft][4 * q4 + 2], S[ft][4 * q4 + 3]};
     } else if (w == 2) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        dstu[(2 * NFT * 4 + q4) * 64 + l] = float4{Z[4 * q4], Z[4 * q4 + 1], Z[4 * q4 + 2], Z[4 * q4 + 3]};
+        dst[ZIDX + q4 * 64 + l] = float4{Z[4 * q4], Z[4 * q4 + 1], Z[4 * q4 + 2], Z[4 * q4 + 3]};
     }
-  } else if (want_state) {
-    if (w < 2) {
-      const int col = 32 * w + lc;
+  } else if (w < 2) {
+    const int col = 32 * w + lc;
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const Feat e = feat(32 * ft + acc_row(j, lh));
-          if (e.can >= 0) a.S[(static_cast<size_t>(bh) * 153 + e.can) * DV + col] = e.wcan * S[ft][j];
-        }
-    } else if (w == 2) {
-      float* z = a.z + static_cast<size_t>(bh) * 153;
+    for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int r = acc_row(j, lh), c = lc;
-        if (r < 16 && c < 16 && r <= c)
-          z[17 + r * 16 - r * (r - 1) / 2 + (c - r)] = (r == c ? 1.f : kSqrt2) * Z[j];
-        else if (r < 16 && c == 16)
-          z[1 + r] = Z[j];
-        else if (r == 16 && c == 16)
-          z[0] = Z[j];
+        const Feat e = feat(32 * ft + acc_row(j, lh));
+        if (e.can >= 0) a.S[(static_cast<size_t>(bh) * 153 + e.can) * DV + col] = e.wcan * S[ft][j];
       }
-    }
-  }
-}
-
-// Per-segment state sums (segments 0..P-2), update only: S += phi(K)^T V and
-// Z += K'^T K' over the segment. Five symmetric waves; wave w owns feature
-// tile w (32 features) for all 64 value columns and builds its own phi(K)^T
-// fragments from an fp32 K'^T in LDS, so the work per wave is a handful of
-// fragments and MFMAs per chunk and the pass runs at the speed of streaming
-// K and V. Chunks of 64 tokens, two LDS buffers, loads two chunks ahead.
-namespace ss {
-constexpr int C = 64;
-constexpr int NW = NFT;                   // one wave per 32-feature tile
-constexpr int NTHR = NW * 64;
-constexpr int KF_P = 72;                  // fp16 K'^T rows 0..17, 64 keys + pad
-constexpr int VT_P = 72;                  // fp16 V^T rows, 64 keys + pad
-constexpr int OFF_KF = 0;
-constexpr int OFF_VT = 18 * KF_P * 2;
-constexpr int BUF = OFF_VT + DV * VT_P * 2;
-constexpr int KITEMS = C * D / 8;         // 16-byte items of K per chunk
-constexpr int ITEMS = KITEMS + C * DV / 8;
-constexpr int PER_T = ITEMS / NTHR;       // items per thread
-static_assert(ITEMS % NTHR == 0, "whole items per thread");
-static_assert(KITEMS % 64 == 0, "K items fill whole waves");
-static_assert(OFF_VT % 16 == 0 && BUF % 16 == 0 && (KF_P * 2) % 16 == 0 && (VT_P * 2) % 16 == 0,
-              "16-byte aligned rows");
-}  // namespace ss
-
-__global__ __launch_bounds__(ss::NTHR) void o2_segsum(PrefillArgs a) {
-  constexpr int C = ss::C, NTHR = ss::NTHR, KF_P = ss::KF_P, VT_P = ss::VT_P, BUF = ss::BUF;
-  constexpr int OFF_KF = ss::OFF_KF, OFF_VT = ss::OFF_VT, KITEMS = ss::KITEMS, PER_T = ss::PER_T;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
-  const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, lc = l & 31, lh = l >> 5;
-  const int PS = a.P - 1;
-  const int unit = blockIdx.x;
-  if (unit >= a.BH * PS) return;
-  const int bh = unit / PS;
-  const int p = unit - bh * PS;
-  const int N = a.N;
-  const int t0 = p * a.L;
-  const int t1 = min(N, t0 + a.L);
-  const int nch = (t1 - t0 + C - 1) / C;
-  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
-  const auto rk = make_rsrc(reinterpret_cast<const __bf16*>(a.k) + (static_cast<size_t>(bh) * N + t0) * D,
-                            seg_rows * D * 2);
-  const auto rv = make_rsrc(reinterpret_cast<const __bf16*>(a.v) + (static_cast<size_t>(bh) * N + t0) * DV,
-                            seg_rows * DV * 2);
-  auto kf = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_KF); };
-  auto vt = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_VT); };
-  for (int i = tid; i < 2 * KF_P; i += NTHR) kf(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
-
-  auto crow = [&](int c, int row) __attribute__((always_inline)) -> uint32_t {
-    const int r = c * C + row;
-    return static_cast<uint32_t>(r < static_cast<int>(seg_rows) ? r : static_cast<int>(seg_rows));
-  };
-  // Item e of a chunk: K rows (two 16-byte items per key) first, then V rows
-  // (eight per key). Thread tid holds items tid + k*NTHR; the K items are
-  // exactly slot 0 of the first KITEMS/64 waves, so the choice between the
-  // two buffers is uniform per wave.
-  auto is_k = [&](int k) __attribute__((always_inline)) { return k == 0 && w < KITEMS / 64; };
-  auto load_item = [&](int c, int k) __attribute__((always_inline)) -> uint4 {
-    const int e = tid + k * NTHR;
-    if (is_k(k)) return bload16(rk, (crow(c, e >> 1) * D + 8 * (e & 1)) * 2);
-    const int j = e - KITEMS;
-    return bload16(rv, (crow(c, j >> 3) * DV + 8 * (j & 7)) * 2);
-  };
-  auto store_item = [&](int c, int b, int k, uint4 x) __attribute__((always_inline)) {
-    const int e = tid + k * NTHR;
-    const f16x8 v = to_h8(__builtin_bit_cast(bf16x8, x));
-    if (is_k(k)) {
-      const int row = e >> 1, half = e & 1;
-      _Float16* kk = kf(b);
+  } else if (w == 2) {
+    float* z = a.z + static_cast<size_t>(bh) * 153;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kk[(8 * half + u) * KF_P + row] = v[u];
-      if (half == 0) kk[16 * KF_P + row] = static_cast<_Float16>(c * C + row < static_cast<int>(seg_rows) ? 1.f : 0.f);
-    } else {
-      const int j = e - KITEMS, row = j >> 3, c8 = j & 7;
-      _Float16* t = vt(b);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) t[(8 * c8 + u) * VT_P + row] = v[u];
-    }
-  };
-
-  uint4 pf[2][PER_T];
-  auto stage = [&](int c, int b, auto slot) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot)::value;
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) {
-      store_item(c, b, k, pf[SL][k]);
-      pf[SL][k] = load_item(c + 2, k);
-    }
-  };
-
-  const Feat fe = feat(32 * w + lc);
-  f32x16 S0 = f32x16{}, S1 = f32x16{}, Z = f32x16{};
-  auto compute = [&](int b) __attribute__((always_inline)) {
-    const _Float16* k = kf(b);
-    const _Float16* v = vt(b);
-#pragma unroll
-    for (int u = 0; u < C / 16; ++u) {
-      const f16x8 af = ldh8(k + fe.i * KF_P + 16 * u + 8 * lh) * ldh8(k + fe.j * KF_P + 16 * u + 8 * lh);
-      S0 = mfma32h(af, ldh8(v + lc * VT_P + 16 * u + 8 * lh), S0);
-      S1 = mfma32h(af, ldh8(v + (32 + lc) * VT_P + 16 * u + 8 * lh), S1);
-      if (w == 0) {
-        // rows 18..31 of K' are zero
-        const f16x8 zf = ldh8(k + (lc < 18 ? lc : 17) * KF_P + 16 * u + 8 * lh);
-        Z = mfma32h(zf, zf, Z);
-      }
-    }
-  };
-
-  using S0_ = std::integral_constant<int, 0>;
-  using S1_ = std::integral_constant<int, 1>;
-#pragma unroll
-  for (int k = 0; k < PER_T; ++k) {
-    pf[0][k] = load_item(0, k);
-    pf[1][k] = load_item(1, k);
-  }
-  stage(0, 0, S0_{});
-  __syncthreads();
-  int i = 0;
-  for (; i + 2 <= nch; i += 2) {
-    stage(i + 1, 1, S1_{});
-    compute(0);
-    __syncthreads();
-    stage(i + 2, 0, S0_{});
-    compute(1);
-    __syncthreads();
-  }
-  if (i < nch) {
-    stage(i + 1, 1, S1_{});
-    compute(0);
-    __syncthreads();
-  }
-
-  // sums in the accumulator layout of the main kernel's state waves
-  float4* dst = reinterpret_cast<float4*>(a.seg) + (static_cast<size_t>(bh) * PS + p) * UNIT_F4;
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    dst[((0 * NFT + w) * 4 + q4) * 64 + l] = float4{S0[4 * q4], S0[4 * q4 + 1], S0[4 * q4 + 2], S0[4 * q4 + 3]};
-    dst[((1 * NFT + w) * 4 + q4) * 64 + l] = float4{S1[4 * q4], S1[4 * q4 + 1], S1[4 * q4 + 2], S1[4 * q4 + 3]};
-  }
-  if (w == 0) {
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      dst[(2 * NFT * 4 + q4) * 64 + l] = float4{Z[4 * q4], Z[4 * q4 + 1], Z[4 * q4 + 2], Z[4 * q4 + 3]};
-  }
-}
-
-// Inclusive prefix over the segments of each head, in place.
-__global__ __launch_bounds__(256) void o2_scan(float4* seg, int BH, int PS) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= static_cast<int64_t>(BH) * UNIT_F4) return;
-  const int64_t bh = e / UNIT_F4, pos = e - bh * UNIT_F4;
-  float4* base = seg + bh * PS * static_cast<int64_t>(UNIT_F4) + pos;
-  float4 acc = base[0];
-  constexpr int B8 = 8;
-  for (int p0 = 1; p0 < PS; p0 += B8) {
-    float4 x[B8];
-#pragma unroll
-    for (int j = 0; j < B8; ++j) x[j] = p0 + j < PS ? base[static_cast<int64_t>(p0 + j) * UNIT_F4] : float4{0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < B8; ++j) {
-      if (p0 + j < PS) {
-        acc.x += x[j].x;
-        acc.y += x[j].y;
-        acc.z += x[j].z;
-        acc.w += x[j].w;
-        base[static_cast<int64_t>(p0 + j) * UNIT_F4] = acc;
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int r = acc_row(j, lh), c = lc;
+      if (r < 16 && c < 16 && r <= c)
+        z[17 + r * 16 - r * (r - 1) / 2 + (c - r)] = (r == c ? 1.f : kSqrt2) * Z[j];
+      else if (r < 16 && c == 16)
+        z[1 + r] = Z[j];
+      else if (r == 16 && c == 16)
+        z[0] = Z[j];
     }
   }
 }
@@ -960,26 +942,25 @@ bool plan(int BH, int N, PrefillPlan* pl) {
   pl->fin_off = off;
   if (pl->P > 1) off += al(static_cast<size_t>(BH) * UNIT_BYTES);
   pl->part_off = off;
+  if (pl->P > 1) {
+    pl->sync_off = off;
+    off += al(static_cast<size_t>(sync_ints(static_cast<int>(BH * pl->P))) * sizeof(int));
+  }
   pl->bytes = off;
   return true;
 }
 
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   hipError_t e;
+  const int units = a.BH * a.P;
   if (a.P > 1) {
-    hipLaunchKernelGGL(o2_segsum, dim3(a.BH * (a.P - 1)), dim3(ss::NTHR), 0, stream, a);
+    hipLaunchKernelGGL(o2_reset, dim3(1), dim3(256), 0, stream, a.sync, sync_ints(units));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.P > 2) {
-      const int64_t n = static_cast<int64_t>(a.BH) * UNIT_F4;
-      hipLaunchKernelGGL(o2_scan, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                         reinterpret_cast<float4*>(a.seg), a.BH, a.P - 1);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
   }
   if (a.o == nullptr || a.out_bf16)
-    hipLaunchKernelGGL((o2_kernel<MAIN, true>), dim3(a.BH * a.P), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((o2_kernel<true>), dim3(units), dim3(NTHR), 0, stream, a);
   else
-    hipLaunchKernelGGL((o2_kernel<MAIN, false>), dim3(a.BH * a.P), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((o2_kernel<false>), dim3(units), dim3(NTHR), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.defer_state && a.S != nullptr) {
     hipLaunchKernelGGL(o2_state_store, dim3(a.BH), dim3(192), 0, stream,
