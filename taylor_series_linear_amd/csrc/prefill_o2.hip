@@ -512,7 +512,7 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       O = mfma32h(cath44(ldh4(vrow + 16 + 4 * lh), ldh4(vrow + 24 + 4 * lh)), P1, O);
       den += __shfl_xor(den, 32);
       den += sm.den(b)[lc];
-      const float rd = 1.f / den;
+      const float rd = __builtin_amdgcn_rcpf(den);
       // normalise, transpose through this wave's LDS area, store rows
       char* st = sm.ostage(m, OB);
       const int rows = min(C, t1 - (t0 + i * C));
