@@ -110,6 +110,11 @@ def stored_traffic():
     return rec["bytes_per_call"] if rec.get("source_hash") == source_hash() else None
 
 
+def feature_dim(d, n_terms):
+    """Width of the symmetric basis: sum over orders m < n of C(d+m-1, m)."""
+    return sum(math.comb(d + m - 1, m) for m in range(n_terms))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -121,8 +126,7 @@ def algorithmic_prefill(w, chunk=CHUNK):
     flops: 4 F (dv+1) for state read-out and update (with the denominator
     column) + (min(c,256)+1)(d+dv+1) for the causal half of the diagonal block.
     """
-    from oracle.taylor_oracle import n_features  # width formula only
-    F = n_features(w.d, w.n_terms)
+    F = feature_dim(w.d, w.n_terms)
     esz = 2 if w.dtype == "bf16" else 4
     th = w.B * w.H * w.N
     bytes_ = th * ((2 * w.d + w.dv) * esz + w.dv * esz)
@@ -214,8 +218,7 @@ def bench_decode(args, torch, tl, W):
     for i in range(16):
         hot(i)
     ms_hot = time_loop(hot, w.steps, torch)
-    from oracle.taylor_oracle import n_features
-    F = n_features(w.d, w.n_terms)
+    F = feature_dim(w.d, w.n_terms)
     state_bytes = 2 * F * (w.dv + 1) * 4 * w.B * w.H   # read + write of S and z
     flops = 4 * F * (w.dv + 1) * w.B * w.H / 2            # 2F(dv+1) per head-step
     return {
@@ -322,7 +325,7 @@ def main():
                  "note": "algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head, c=32"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                     "kernel": "one taylor_attn_prefill call: o2 segment sums + prefix scan + main (3 launches)",
+                     "kernel": "one taylor_attn_prefill call: flag reset + single-pass o2 kernel (2 launches)",
                      "launch_us": ms * 1e3, "algorithmic_bytes_per_launch": bytes_},
     }
     if args.only != "prefill" and not args.no_decode:
