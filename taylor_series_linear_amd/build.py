@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtaylor_attn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "prefill.hip", "prefill_o2.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefill.hip", "prefill_o2.hip", "prefill_w2.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -178,7 +178,7 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
   args.S = S;
   args.z = z;
   char* ws = static_cast<char*>(workspace);
-  args.seg = p.P > 1 ? reinterpret_cast<float*>(ws + p.seg_off) : nullptr;
+  args.seg = p.fin_off > p.seg_off ? reinterpret_cast<float*>(ws + p.seg_off) : nullptr;
   args.fin = p.P > 1 ? reinterpret_cast<float*>(ws + p.fin_off) : nullptr;
   args.part = p.bytes > p.part_off ? reinterpret_cast<float*>(ws + p.part_off) : nullptr;
   args.sync = p.sync_off > 0 ? reinterpret_cast<int*>(ws + p.sync_off) : nullptr;

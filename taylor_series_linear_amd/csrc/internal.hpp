@@ -58,6 +58,12 @@ bool plan(int BH, int N, PrefillPlan* plan);
 hipError_t launch(const PrefillArgs& a, hipStream_t stream);
 }  // namespace o2
 
+// Order-2, d = 64, dv = 64, bf16 prefill (prefill_w2.hip).
+namespace w2 {
+bool plan(int BH, int N, PrefillPlan* plan);
+hipError_t launch(const PrefillArgs& a, hipStream_t stream);
+}  // namespace w2
+
 struct DecodeArgs {
   const void* q;
   const void* k;

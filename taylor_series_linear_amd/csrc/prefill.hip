@@ -793,7 +793,6 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(64, 64, 1, false, 32, 64, true)         \
   X(64, 16, 3, true, 544, 32, false)        \
   X(64, 16, 3, false, 128, 32, false)       \
-  X(64, 64, 3, true, 544, 32, false)        \
   X(64, 64, 3, false, 128, 32, false)
 
 // Sequence split for the generic kernels: enough workgroups (heads x
@@ -828,12 +827,15 @@ static void plan_cfg(int BH, int N, PrefillPlan* p) {
   p->bytes = off;
 }
 
+static bool is_w2(int d, int dv, int n_terms, bool bf16) { return d == 64 && dv == 64 && n_terms == 3 && bf16; }
+
 static bool is_o2(int d, int dv, int n_terms, bool bf16) {
   return d == 16 && dv == 64 && n_terms == 3 && bf16;
 }
 
 bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillPlan* plan) {
   if (is_o2(d, dv, n_terms, bf16)) return o2::plan(BH, N, plan);
+  if (is_w2(d, dv, n_terms, bf16)) return w2::plan(BH, N, plan);
 #define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
   if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_) {             \
     plan_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(BH, N, plan);          \
@@ -847,6 +849,7 @@ bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillP
 hipError_t prefill_launch(int d, int dv, int n_terms, bool bf16, const PrefillArgs& a,
                           hipStream_t stream) {
   if (is_o2(d, dv, n_terms, bf16)) return o2::launch(a, stream);
+  if (is_w2(d, dv, n_terms, bf16)) return w2::launch(a, stream);
 #define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
   if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_)               \
     return launch_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(a, stream);
