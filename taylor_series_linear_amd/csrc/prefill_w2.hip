@@ -88,6 +88,20 @@ __host__ __device__ constexpr Slot slot_info(int s) {
   return Slot{S_Z, 0, 0, i == 2 ? 1 : 0, i == 0 ? 0 : 1};
 }
 
+// a range shared by every state slot of wave w (all of them pair classes),
+// or -1
+__host__ __device__ constexpr int uniform_abase(int w) {
+  int ab = -1;
+  for (int s = slot_begin(w); s < slot_begin(w + 1); ++s) {
+    const Slot t = slot_info(s);
+    if (t.kind == S_Z) continue;
+    if (t.kind != S_CLASS) return -1;
+    if (ab >= 0 && t.abase != ab) return -1;
+    ab = t.abase;
+  }
+  return ab;
+}
+
 // Canonical index and weight of state row r of state slot s.
 struct Feat {
   int can;      // canonical feature, -1 for a zero slot
@@ -122,7 +136,8 @@ static_assert(basis_is_bijective(), "internal basis covers the canonical one onc
 // LDS layout of one chunk buffer (bytes). Row pitches keep 16-byte alignment
 // and put consecutive rows on different banks.
 constexpr int QRP = 104;   // raw q (bf16): q[0..63], 1, zeros (Gram block 2)
-constexpr int QFP = 168;   // q/a (fp16): q/a[0..63], q/a[0..31], ones x32, zeros x32
+constexpr int QFP = 164;   // q/a (fp16): q/a[0..63], q/a[0..31], ones x32, zeros x32;
+                           // 82-dword rows: 8-byte reads of 32 rows hit 64 banks
 constexpr int KRP = 72;    // raw k rows (bf16)
 constexpr int KTP = 40;    // K'^T rows (fp16): 0..63 coordinates, 64..95 = 0..31, 96 valid, 97 zero
 constexpr int VTP = 40;    // V^T rows (fp16), this workgroup's 32 columns
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   // item of this thread: threads 0..255 a Q item, 256..511 a K item (row
   // it >> 3, coordinates 8 (it & 7) .. +8); threads 0..127 also a V item
   // (row tid >> 2, this half's columns 8 (tid & 3) .. +8)
-  const bool is_q = tid < 256;
+  const bool is_q = __builtin_amdgcn_readfirstlane(tid) < 256;
   const int it = is_q ? tid : tid - 256;
   const int irow = it >> 3, ic8 = it & 7;
   const bool has_v = tid < 128;
@@ -272,15 +287,21 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   auto load_v = [&](int c) __attribute__((always_inline)) -> uint4 {
     return bload16(rv, (crow(c, vrow) * DV + DH * hv + 8 * vc4) * 2);
   };
-  uint4 ra[2], rvv[2];
+  uint4 ra[1], rvv[1];  // one chunk ahead: the chunk's compute covers the load latency
   auto stage = [&](int c, int b, auto slot) __attribute__((always_inline)) {
     constexpr int SL = decltype(slot)::value;
+    static_assert(SL == 0, "one ring slot");
     const bf16x8 x = __builtin_bit_cast(bf16x8, ra[SL]);
     if (MODE == MAIN && is_q) {
       *reinterpret_cast<bf16x8*>(qr(b) + irow * QRP + 8 * ic8) = x;
       const f16x8 h = b2h(x, inv_a);
-      *reinterpret_cast<f16x8*>(qf(b) + irow * QFP + 8 * ic8) = h;
-      if (ic8 < 4) *reinterpret_cast<f16x8*>(qf(b) + irow * QFP + D + 8 * ic8) = h;
+      const f16x4 h0{h[0], h[1], h[2], h[3]}, h1{h[4], h[5], h[6], h[7]};
+      *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + 8 * ic8) = h0;
+      *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + 8 * ic8 + 4) = h1;
+      if (ic8 < 4) {
+        *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + D + 8 * ic8) = h0;
+        *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + D + 8 * ic8 + 4) = h1;
+      }
     } else if (!is_q) {
       if (MODE == MAIN) *reinterpret_cast<bf16x8*>(kr(b) + irow * KRP + 8 * ic8) = x;
       const f16x8 h = b2h(x, 1.f);
@@ -299,8 +320,8 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) t[(8 * vc4 + u) * VTP + vrow] = h[u];
     }
-    ra[SL] = load_a(c + 2);
-    if (has_v) rvv[SL] = load_v(c + 2);
+    ra[SL] = load_a(c + 1);
+    if (has_v) rvv[SL] = load_v(c + 1);
   };
 
   // per-chunk compute ---------------------------------------------------------
@@ -318,6 +339,20 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     const __bf16* QR = qr(b) + lc * QRP;
     f32x16 O = f32x16{};
     float dpart = 0.f;
+    // operands shared by the chunk: V^T fragments; and, when every state
+    // slot of the wave covers the same a range, the a-side rows of both
+    // feature fragments
+    constexpr int UAB = uniform_abase(W);
+    f16x8 bv[2], aq[2], kx[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bv[ks] = lds<f16x8>(V + lc * VTP + 16 * ks + 8 * lh);
+      if constexpr (UAB >= 0) {
+        const int o = UAB + 16 * ks + 4 * lh;
+        aq[ks] = cat(lds<f16x4>(QF + o), lds<f16x4>(QF + o + 8));
+        kx[ks] = lds<f16x8>(K + (UAB + lc) * KTP + 16 * ks + 8 * lh);
+      }
+    }
     static_for<0, NSW>([&](auto sli) {
       constexpr int sl = decltype(sli)::value;
       constexpr Slot t = slot_info(SB + sl);
@@ -330,8 +365,12 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             const int o = 16 * ks + 4 * lh;
-            f16x8 ph = cat(lds<f16x4>(QF + acol + o), lds<f16x4>(QF + acol + o + 8)) *
-                       cat(lds<f16x4>(QF + bcol + o), lds<f16x4>(QF + bcol + o + 8));
+            f16x8 qa;
+            if constexpr (UAB >= 0)
+              qa = aq[ks];
+            else
+              qa = cat(lds<f16x4>(QF + acol + o), lds<f16x4>(QF + acol + o + 8));
+            f16x8 ph = qa * cat(lds<f16x4>(QF + bcol + o), lds<f16x4>(QF + bcol + o + 8));
             if constexpr (t.kind == S_CLASS && t.koff == 0) ph = ph * halfh;
             bf16x8 sa;
 #pragma unroll
@@ -344,9 +383,12 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
         const int brow = t.kind == S_CLASS ? t.abase + lc + t.koff : ROW_VALID;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 x = lds<f16x8>(K + arow * KTP + 16 * ks + 8 * lh);
-          const f16x8 y = lds<f16x8>(K + brow * KTP + 16 * ks + 8 * lh);
-          acc[sl] = mfma32h(x * y, lds<f16x8>(V + lc * VTP + 16 * ks + 8 * lh), acc[sl]);
+          f16x8 x;
+          if constexpr (UAB >= 0)
+            x = kx[ks];
+          else
+            x = lds<f16x8>(K + arow * KTP + 16 * ks + 8 * lh);
+          acc[sl] = mfma32h(x * lds<f16x8>(K + brow * KTP + 16 * ks + 8 * lh), bv[ks], acc[sl]);
         }
       } else {
         if (out) {
@@ -502,11 +544,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     // chunk loop: iteration i stages chunk i+1, computes chunk i and
     // finishes chunk i-1
     ra[0] = load_a(0);
-    ra[1] = load_a(1);
-    if (has_v) {
-      rvv[0] = load_v(0);
-      rvv[1] = load_v(1);
-    }
+    if (has_v) rvv[0] = load_v(0);
     stage(0, 0, S0_{});
     __syncthreads();
     auto iter = [&](int i, auto slot) __attribute__((always_inline)) {
@@ -517,10 +555,10 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     };
     int i = 0;
     for (; i + 2 <= nch; i += 2) {
-      iter(i, S1_{});
+      iter(i, S0_{});
       iter(i + 1, S0_{});
     }
-    if (i < nch) iter(i, S1_{});
+    if (i < nch) iter(i, S0_{});
     if (want_out && nch > 0) finalize(nch - 1);
 
     // results
