@@ -95,7 +95,16 @@ struct PCfg {
   static constexpr int OFF_PK = OFF_PQ + C * PQ * ES;
   static constexpr int OFF_P = OFF_PK + FS * PK * ES;
   static constexpr int OFF_DEN = OFF_P + C * PP * ES;
-  static constexpr int LDS = OFF_DEN + C * 4;
+  // table-driven generator: per-token factor tables T^T [TE][TP] fp32 for the
+  // query and the key side (1, the coordinates, and for orders above 2 the
+  // pair products), token-contiguous
+  static constexpr bool PAIRS = NT > 3;
+  static constexpr int TE = UNROLL ? 0 : 1 + D + (PAIRS ? D * (D + 1) / 2 : 0);
+  static constexpr int TP = C + 4;
+  static constexpr int OFF_TQ = OFF_DEN + C * 4;
+  static constexpr int OFF_TK = OFF_TQ + TE * TP * 4;
+  static constexpr int LDS = OFF_TK + TE * TP * 4;
+  static_assert(NT <= 5, "features are products of two table entries up to order 4");
   static_assert(FS % 32 == 0 && C % 32 == 0 && DV % 16 == 0, "tile multiples");
   static_assert(D % 16 == 0, "head dim multiple of 16");
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -208,6 +217,130 @@ __device__ __forceinline__ void gen_unrolled(int w, const float (&x)[Cfg::D], ty
 
 template <int D, int NT>
 __device__ const PackedTable<D, NT> g_ptab = make_packed<D, NT>();
+
+// Table-driven generation. Every feature of order m <= 4 is the product of
+// two entries of a per-token factor table T = [1, x_0..x_{d-1}, x_i x_j
+// (i <= j, lexicographic; orders above 2 only)] times a constant:
+//   m = 0: T[0] T[0],  m = 1: T[0] T[1+i],  m = 2: T[0] T[pair(i,j)] (or
+//   T[1+i] T[1+j] without pairs),  m = 3: T[pair(i,j)] T[1+k],
+//   m = 4: T[pair(i,j)] T[pair(k,l)].
+// The tables are built once per chunk; each lane owns a feature and reads
+// both of its rows 16 bytes at a time.
+template <int D>
+__host__ __device__ constexpr int tab_pair(int i, int j) {
+  return 1 + D + i * D - i * (i - 1) / 2 + (j - i);
+}
+
+struct TabFeat {
+  int oa, ob;  // float offsets of the two table rows
+  float cq;    // query side: sqrt-multinomial * alpha_m (1 / (m! a^m))
+  float ck;    // key side: sqrt-multinomial
+};
+
+template <class Cfg>
+__device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
+  constexpr int D = Cfg::D, TP = Cfg::TP;
+  TabFeat t{0, 0, 0.f, 0.f};
+  if (f >= Cfg::F) return t;
+  const PackedFeature e = g_ptab<D, Cfg::NT>.e[f];
+  const int m = static_cast<int>(e.m);
+  const int i0 = e.idx & 255, i1 = (e.idx >> 8) & 255, i2 = (e.idx >> 16) & 255, i3 = e.idx >> 24;
+  int a = 0, b = 0;
+  if (m == 1) {
+    b = 1 + i0;
+  } else if (m == 2) {
+    if constexpr (Cfg::PAIRS) {
+      b = tab_pair<D>(i0, i1);
+    } else {
+      a = 1 + i0;
+      b = 1 + i1;
+    }
+  } else if (m == 3) {
+    a = tab_pair<D>(i0, i1);
+    b = 1 + i2;
+  } else if (m == 4) {
+    a = tab_pair<D>(i0, i1);
+    b = tab_pair<D>(i2, i3);
+  }
+  t.oa = a * TP;
+  t.ob = b * TP;
+  t.ck = e.w;
+  float cq = e.w * e.inv_mfact;
+  for (int j = 0; j < m; ++j) cq *= inv_a;
+  t.cq = cq;
+  return t;
+}
+
+// Pair rows of both tables from their coordinate rows (rows 1..D, written
+// while staging): T[pair(i,j)][t] = T[1+i][t] T[1+j][t], 4 tokens at a time.
+template <class Cfg>
+__device__ __forceinline__ void build_pairs(int tid, float* TQ, float* TK, bool qside) {
+  constexpr int D = Cfg::D, C = Cfg::C, TP = Cfg::TP, NPAIR = D * (D + 1) / 2;
+  for (int k = tid; k < 2 * NPAIR; k += Cfg::NTHR) {
+    const bool isq = k < NPAIR;
+    if (isq && !qside) continue;
+    float* T = isq ? TQ : TK;
+    int r = isq ? k : k - NPAIR, pi = 0;
+    while (r >= D - pi) {
+      r -= D - pi;
+      ++pi;
+    }
+    const f32x4* xi = reinterpret_cast<const f32x4*>(T + (1 + pi) * TP);
+    const f32x4* xj = reinterpret_cast<const f32x4*>(T + (1 + pi + r) * TP);
+    f32x4* dst = reinterpret_cast<f32x4*>(T + tab_pair<D>(pi, pi + r) * TP);
+#pragma unroll
+    for (int u = 0; u < C / 4; ++u) dst[u] = xi[u] * xj[u];
+  }
+}
+
+// Query side: phi~(Q) [C x FS], query-major. Key side: phi(K)^T [FS x C].
+template <class Cfg, bool QSIDE>
+__device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, const float* T,
+                                        typename Cfg::E* dst) {
+  using E = typename Cfg::E;
+  constexpr int NB = (Cfg::FS + 63) / 64, NBW = (NB + Cfg::NW - 1) / Cfg::NW, C = Cfg::C;
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int blk = w + Cfg::NW * j;
+    const int fl = 64 * blk + lane;
+    if (blk >= NB || fl >= Cfg::FS) continue;
+    const float* ta = T + tf[j].oa;
+    const float* tb = T + tf[j].ob;
+    if constexpr (QSIDE) {
+      const float cf = tf[j].cq;
+#pragma unroll
+      for (int t0 = 0; t0 < C; t0 += 4) {
+        const f32x4 va = *reinterpret_cast<const f32x4*>(ta + t0);
+        const f32x4 vb = *reinterpret_cast<const f32x4*>(tb + t0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[(t0 + u) * Cfg::PQ + fl] = Cfg::M::cvt(va[u] * vb[u] * cf);
+      }
+    } else {
+      const float cf = tf[j].ck;
+#pragma unroll
+      for (int t0 = 0; t0 < C; t0 += 8) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ta + t0);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ta + t0 + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(tb + t0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(tb + t0 + 4);
+        const f32x4 p0 = a0 * b0 * cf, p1 = a1 * b1 * cf;
+        E* out = dst + fl * Cfg::PK + t0;
+        if constexpr (Cfg::BF16) {
+          bf16x8 pk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            pk[u] = static_cast<__bf16>(p0[u]);
+            pk[u + 4] = static_cast<__bf16>(p1[u]);
+          }
+          *reinterpret_cast<bf16x8*>(out) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(out) = p0;
+          *reinterpret_cast<f32x4*>(out + 4) = p1;
+        }
+      }
+    }
+  }
+}
 
 // Lanes own features, loop over the chunk's tokens; x rows are read from LDS
 // (all lanes read the same row: broadcast).
@@ -440,6 +573,19 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
 
   const float inv_a = a.inv_a;
 
+  // table-driven generator: this lane's features (fixed for the kernel)
+  constexpr int NBW = ((Cfg::FS + 63) / 64 + NW - 1) / NW;
+  TabFeat tf[NBW];
+  float* sTQ = reinterpret_cast<float*>(smem + Cfg::OFF_TQ);
+  float* sTK = reinterpret_cast<float*>(smem + Cfg::OFF_TK);
+  if constexpr (!Cfg::UNROLL) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) tf[j] = tab_feat<Cfg>(f0 + 64 * (w + NW * j) + lane, inv_a);
+    // row 0 of both tables is the constant 1 (also for rows past the end of
+    // the sequence: their values and ones-row entries are zero)
+    for (int t = tid; t < 2 * Cfg::C; t += Cfg::NTHR) (t < Cfg::C ? sTQ : sTK)[t % Cfg::C] = 1.f;
+  }
+
   // ---- chunk loop ------------------------------------------------------------
   // Global loads run one chunk ahead: the next chunk's Q, K and V rows are
   // fetched into registers (16 bytes per item) while the current chunk is in
@@ -473,18 +619,32 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  // Q, K row-major; V transposed (key-contiguous) with the ones row below it.
+  // Q, K row-major (and, for the table-driven generator, transposed into the
+  // coordinate rows of the factor tables); V transposed (key-contiguous) with
+  // the ones row below it.
   auto stage = [&](int nvv) {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int i = tid + s * Cfg::NTHR;
       if (i < QB) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
-        if (want_out) *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = pf[s];
+        if (want_out) {
+          *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = pf[s];
+          if constexpr (!Cfg::UNROLL) {
+            const E* e = reinterpret_cast<const E*>(&pf[s]);
+#pragma unroll
+            for (int u = 0; u < EV; ++u) sTQ[(1 + col + u) * Cfg::TP + row] = static_cast<float>(e[u]);
+          }
+        }
       } else if (i < QB + NQI) {
         const int j = i - QB;
         const int row = j / (D / EV), col = (j % (D / EV)) * EV;
         *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = pf[s];
+        if constexpr (!Cfg::UNROLL) {
+          const E* e = reinterpret_cast<const E*>(&pf[s]);
+#pragma unroll
+          for (int u = 0; u < EV; ++u) sTK[(1 + col + u) * Cfg::TP + row] = static_cast<float>(e[u]);
+        }
       } else if (i < NIT) {
         const int j = i - QB - NQI;
         const int row = j / (DV / EV), col = (j % (DV / EV)) * EV;
@@ -522,8 +682,12 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         }
       }
     } else {
-      if (want_out) gen_table<Cfg, true>(w, lane, f0, sQ, sPQ, inv_a);
-      if (do_update) gen_table<Cfg, false>(w, lane, f0, sK, sPK, inv_a);
+      if constexpr (Cfg::PAIRS) {
+        build_pairs<Cfg>(tid, sTQ, sTK, want_out);
+        __syncthreads();
+      }
+      if (want_out) gen_tab<Cfg, true>(w, lane, tf, sTQ, sPQ);
+      if (do_update) gen_tab<Cfg, false>(w, lane, tf, sTK, sPK);
     }
     if (want_out && gsl == 0) {
       static_for<0, NW>([&](auto ri) {
