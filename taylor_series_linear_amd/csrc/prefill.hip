@@ -101,9 +101,16 @@ struct PCfg {
   static constexpr bool PAIRS = NT > 3;
   static constexpr int TE = UNROLL ? 0 : 1 + D + (PAIRS ? D * (D + 1) / 2 : 0);
   static constexpr int TP = C + 4;
+  // key side of the table-driven generator: bf16 inputs keep the key table,
+  // phi(K)^T and the update contraction in fp16 (keys scaled by KS, so
+  // features of order m carry KS^m), fp32 inputs in fp32
+  static constexpr bool KH = BF16 && !UNROLL;
+  static constexpr float KS = KH ? 0.5f : 1.f;
+  static constexpr int KES = KH ? 2 : ES;
+  static constexpr int TPK = KH ? C + 8 : C + 4;
   static constexpr int OFF_TQ = OFF_DEN + C * 4;
   static constexpr int OFF_TK = OFF_TQ + TE * TP * 4;
-  static constexpr int LDS = OFF_TK + TE * TP * 4;
+  static constexpr int LDS = OFF_TK + TE * TPK * KES;
   static_assert(NT <= 5, "features are products of two table entries up to order 4");
   static_assert(FS % 32 == 0 && C % 32 == 0 && DV % 16 == 0, "tile multiples");
   static_assert(D % 16 == 0, "head dim multiple of 16");
@@ -231,16 +238,21 @@ __host__ __device__ constexpr int tab_pair(int i, int j) {
   return 1 + D + i * D - i * (i - 1) / 2 + (j - i);
 }
 
+// The key side carries plain products of the scaled keys, u(KS k); the
+// query side carries every weight, w^2 alpha_m / KS^m with w the
+// sqrt-multinomial and alpha_m = 1 / (m! a^m), so that the read-out equals
+// the canonical one. Internal states relate to canonical ones by
+// canonical = (w / KS^m) internal.
 struct TabFeat {
-  int oa, ob;  // float offsets of the two table rows
-  float cq;    // query side: sqrt-multinomial * alpha_m (1 / (m! a^m))
-  float ck;    // key side: sqrt-multinomial
+  int oa, ob;  // offsets (elements) of the two table rows, query table
+  int ka, kb;  // the same rows in the key table
+  float cq;    // query-side weight
 };
 
 template <class Cfg>
 __device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
   constexpr int D = Cfg::D, TP = Cfg::TP;
-  TabFeat t{0, 0, 0.f, 0.f};
+  TabFeat t{0, 0, 0, 0, 0.f};
   if (f >= Cfg::F) return t;
   const PackedFeature e = g_ptab<D, Cfg::NT>.e[f];
   const int m = static_cast<int>(e.m);
@@ -264,49 +276,101 @@ __device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
   }
   t.oa = a * TP;
   t.ob = b * TP;
-  t.ck = e.w;
-  float cq = e.w * e.inv_mfact;
-  for (int j = 0; j < m; ++j) cq *= inv_a;
+  t.ka = a * Cfg::TPK;
+  t.kb = b * Cfg::TPK;
+  float cq = e.w * e.w * e.inv_mfact;
+  for (int j = 0; j < m; ++j) cq *= inv_a / Cfg::KS;
   t.cq = cq;
   return t;
 }
 
-// Pair rows of both tables from their coordinate rows (rows 1..D, written
-// while staging): T[pair(i,j)][t] = T[1+i][t] T[1+j][t], 4 tokens at a time.
+// canonical / internal state row scale of feature f (1 for the unrolled
+// generators, which weight both sides)
 template <class Cfg>
-__device__ __forceinline__ void build_pairs(int tid, float* TQ, float* TK, bool qside) {
-  constexpr int D = Cfg::D, C = Cfg::C, TP = Cfg::TP, NPAIR = D * (D + 1) / 2;
-  for (int k = tid; k < 2 * NPAIR; k += Cfg::NTHR) {
-    const bool isq = k < NPAIR;
-    if (isq && !qside) continue;
-    float* T = isq ? TQ : TK;
-    int r = isq ? k : k - NPAIR, pi = 0;
-    while (r >= D - pi) {
-      r -= D - pi;
-      ++pi;
-    }
-    const f32x4* xi = reinterpret_cast<const f32x4*>(T + (1 + pi) * TP);
-    const f32x4* xj = reinterpret_cast<const f32x4*>(T + (1 + pi + r) * TP);
-    f32x4* dst = reinterpret_cast<f32x4*>(T + tab_pair<D>(pi, pi + r) * TP);
-#pragma unroll
-    for (int u = 0; u < C / 4; ++u) dst[u] = xi[u] * xj[u];
+__device__ __forceinline__ float state_scale(int f) {
+  if constexpr (Cfg::UNROLL) {
+    return 1.f;
+  } else {
+    const PackedFeature e = g_ptab<Cfg::D, Cfg::NT>.e[f];
+    float sc = e.w;
+    for (int j = 0; j < static_cast<int>(e.m); ++j) sc *= 1.f / Cfg::KS;
+    return sc;
   }
 }
 
-// Query side: phi~(Q) [C x FS], query-major. Key side: phi(K)^T [FS x C].
-template <class Cfg, bool QSIDE>
-__device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, const float* T,
-                                        typename Cfg::E* dst) {
-  using E = typename Cfg::E;
+// Pair rows of both tables from their coordinate rows (rows 1..D, written
+// while staging): T[pair(i,j)][t] = T[1+i][t] T[1+j][t], 16 bytes at a time.
+// Thread tid handles pairs tid, tid + NTHR, ... of the 2 * NPAIR (query
+// pairs first); their coordinates are decoded once per kernel.
+template <class Cfg>
+struct PairJobs {
+  static constexpr int NPAIR = Cfg::D * (Cfg::D + 1) / 2;
+  static constexpr int N = Cfg::PAIRS ? (2 * NPAIR + Cfg::NTHR - 1) / Cfg::NTHR : 0;
+  int ij[N > 0 ? N : 1];  // i | j << 8, or -1
+};
+template <class Cfg>
+__device__ __forceinline__ PairJobs<Cfg> pair_jobs(int tid) {
+  constexpr int D = Cfg::D, NPAIR = PairJobs<Cfg>::NPAIR;
+  PairJobs<Cfg> pj;
+#pragma unroll
+  for (int n = 0; n < PairJobs<Cfg>::N; ++n) {
+    const int k = tid + n * Cfg::NTHR;
+    pj.ij[n] = -1;
+    if (k < 2 * NPAIR) {
+      int r = k < NPAIR ? k : k - NPAIR, pi = 0;
+      while (r >= D - pi) {
+        r -= D - pi;
+        ++pi;
+      }
+      pj.ij[n] = pi | (pi + r) << 8;
+    }
+  }
+  return pj;
+}
+template <class Cfg, class KE>
+__device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, float* TQ, KE* TK, bool qside) {
+  constexpr int D = Cfg::D, C = Cfg::C, NPAIR = PairJobs<Cfg>::NPAIR;
+#pragma unroll
+  for (int n = 0; n < PairJobs<Cfg>::N; ++n) {
+    const int k = tid + n * Cfg::NTHR;
+    const int ij = pj.ij[n];
+    if (ij < 0) continue;
+    const int pi = ij & 255, pjj = ij >> 8;
+    if (k < NPAIR) {
+      if (!qside) continue;
+      const f32x4* xi = reinterpret_cast<const f32x4*>(TQ + (1 + pi) * Cfg::TP);
+      const f32x4* xj = reinterpret_cast<const f32x4*>(TQ + (1 + pjj) * Cfg::TP);
+      f32x4* dst = reinterpret_cast<f32x4*>(TQ + tab_pair<D>(pi, pjj) * Cfg::TP);
+#pragma unroll
+      for (int u = 0; u < C / 4; ++u) dst[u] = xi[u] * xj[u];
+    } else if constexpr (Cfg::KH) {
+      const f16x8* xi = reinterpret_cast<const f16x8*>(TK + (1 + pi) * Cfg::TPK);
+      const f16x8* xj = reinterpret_cast<const f16x8*>(TK + (1 + pjj) * Cfg::TPK);
+      f16x8* dst = reinterpret_cast<f16x8*>(TK + tab_pair<D>(pi, pjj) * Cfg::TPK);
+#pragma unroll
+      for (int u = 0; u < C / 8; ++u) dst[u] = xi[u] * xj[u];
+    } else {
+      const f32x4* xi = reinterpret_cast<const f32x4*>(TK + (1 + pi) * Cfg::TPK);
+      const f32x4* xj = reinterpret_cast<const f32x4*>(TK + (1 + pjj) * Cfg::TPK);
+      f32x4* dst = reinterpret_cast<f32x4*>(TK + tab_pair<D>(pi, pjj) * Cfg::TPK);
+#pragma unroll
+      for (int u = 0; u < C / 4; ++u) dst[u] = xi[u] * xj[u];
+    }
+  }
+}
+
+// Query side: phi~(Q) [C x FS], query-major. Key side: u(KS K)^T [FS x C].
+template <class Cfg, bool QSIDE, class TE_, class DE>
+__device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, const TE_* T, DE* dst) {
   constexpr int NB = (Cfg::FS + 63) / 64, NBW = (NB + Cfg::NW - 1) / Cfg::NW, C = Cfg::C;
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int blk = w + Cfg::NW * j;
     const int fl = 64 * blk + lane;
     if (blk >= NB || fl >= Cfg::FS) continue;
-    const float* ta = T + tf[j].oa;
-    const float* tb = T + tf[j].ob;
     if constexpr (QSIDE) {
+      const float* ta = T + tf[j].oa;
+      const float* tb = T + tf[j].ob;
       const float cf = tf[j].cq;
 #pragma unroll
       for (int t0 = 0; t0 < C; t0 += 4) {
@@ -315,29 +379,20 @@ __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, cons
 #pragma unroll
         for (int u = 0; u < 4; ++u) dst[(t0 + u) * Cfg::PQ + fl] = Cfg::M::cvt(va[u] * vb[u] * cf);
       }
+    } else if constexpr (Cfg::KH) {
+      const TE_* ta = T + tf[j].ka;
+      const TE_* tb = T + tf[j].kb;
+#pragma unroll
+      for (int t0 = 0; t0 < C; t0 += 8)
+        *reinterpret_cast<f16x8*>(dst + fl * Cfg::PK + t0) =
+            *reinterpret_cast<const f16x8*>(ta + t0) * *reinterpret_cast<const f16x8*>(tb + t0);
     } else {
-      const float cf = tf[j].ck;
+      const TE_* ta = T + tf[j].ka;
+      const TE_* tb = T + tf[j].kb;
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 8) {
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(ta + t0);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(ta + t0 + 4);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(tb + t0);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(tb + t0 + 4);
-        const f32x4 p0 = a0 * b0 * cf, p1 = a1 * b1 * cf;
-        E* out = dst + fl * Cfg::PK + t0;
-        if constexpr (Cfg::BF16) {
-          bf16x8 pk;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            pk[u] = static_cast<__bf16>(p0[u]);
-            pk[u + 4] = static_cast<__bf16>(p1[u]);
-          }
-          *reinterpret_cast<bf16x8*>(out) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(out) = p0;
-          *reinterpret_cast<f32x4*>(out + 4) = p1;
-        }
-      }
+      for (int t0 = 0; t0 < C; t0 += 4)
+        *reinterpret_cast<f32x4*>(dst + fl * Cfg::PK + t0) =
+            *reinterpret_cast<const f32x4*>(ta + t0) * *reinterpret_cast<const f32x4*>(tb + t0);
     }
   }
 }
@@ -491,7 +546,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   E* sK = reinterpret_cast<E*>(smem + Cfg::OFF_K);
   E* sV = reinterpret_cast<E*>(smem + Cfg::OFF_V);
   E* sPQ = reinterpret_cast<E*>(smem + Cfg::OFF_PQ);
-  E* sPK = reinterpret_cast<E*>(smem + Cfg::OFF_PK);
+  using KE = std::conditional_t<Cfg::KH, _Float16, E>;  // phi(K)^T and key-table element
+  KE* sPK = reinterpret_cast<KE*>(smem + Cfg::OFF_PK);
   E* sP = reinterpret_cast<E*>(smem + Cfg::OFF_P);
   float* sDen = reinterpret_cast<float*>(smem + Cfg::OFF_DEN);
 
@@ -544,6 +600,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
               val = a.S0[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c];
             else if (c == 0)
               val = a.z0[static_cast<size_t>(bh) * Cfg::F + f];
+            if constexpr (!Cfg::UNROLL) val /= state_scale<Cfg>(f);
           }
           S[ft][i] = val;
         }
@@ -577,13 +634,17 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   constexpr int NBW = ((Cfg::FS + 63) / 64 + NW - 1) / NW;
   TabFeat tf[NBW];
   float* sTQ = reinterpret_cast<float*>(smem + Cfg::OFF_TQ);
-  float* sTK = reinterpret_cast<float*>(smem + Cfg::OFF_TK);
+  KE* sTK = reinterpret_cast<KE*>(smem + Cfg::OFF_TK);
+  const PairJobs<Cfg> pj = pair_jobs<Cfg>(tid);
   if constexpr (!Cfg::UNROLL) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) tf[j] = tab_feat<Cfg>(f0 + 64 * (w + NW * j) + lane, inv_a);
     // row 0 of both tables is the constant 1 (also for rows past the end of
     // the sequence: their values and ones-row entries are zero)
-    for (int t = tid; t < 2 * Cfg::C; t += Cfg::NTHR) (t < Cfg::C ? sTQ : sTK)[t % Cfg::C] = 1.f;
+    for (int t = tid; t < Cfg::C; t += Cfg::NTHR) {
+      sTQ[t] = 1.f;
+      sTK[t] = static_cast<KE>(1.f);
+    }
   }
 
   // ---- chunk loop ------------------------------------------------------------
@@ -643,7 +704,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         if constexpr (!Cfg::UNROLL) {
           const E* e = reinterpret_cast<const E*>(&pf[s]);
 #pragma unroll
-          for (int u = 0; u < EV; ++u) sTK[(1 + col + u) * Cfg::TP + row] = static_cast<float>(e[u]);
+          for (int u = 0; u < EV; ++u) sTK[(1 + col + u) * Cfg::TPK + row] = static_cast<KE>(static_cast<float>(e[u]) * Cfg::KS);
         }
       } else if (i < NIT) {
         const int j = i - QB - NQI;
@@ -683,7 +744,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       }
     } else {
       if constexpr (Cfg::PAIRS) {
-        build_pairs<Cfg>(tid, sTQ, sTK, want_out);
+        build_pairs<Cfg>(tid, pj, sTQ, sTK, want_out);
         __syncthreads();
       }
       if (want_out) gen_tab<Cfg, true>(w, lane, tf, sTQ, sPQ);
@@ -796,18 +857,41 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     if (do_update) {
       // S[:, dv tile w] += phi(K)^T [V,1][:, dv tile w]; the phi(K)^T
       // fragments of feature tile ft+1 are fetched before the MFMAs of ft.
-      frag ak[2][KSC];
+      if constexpr (Cfg::KH) {
+        // fp16 contraction: u(KS K)^T from the key table, [V,1] converted
+        f16x8 bvh[KSC], ak[2][KSC];
 #pragma unroll
-      for (int u = 0; u < KSC; ++u) ak[0][u] = lds_frag8(sPK + c * Cfg::PK + 32 * u + 8 * g4);
+        for (int u = 0; u < KSC; ++u)
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        if (ft + 1 < FT) {
+          for (int j = 0; j < 8; ++j) bvh[u][j] = static_cast<_Float16>(static_cast<float>(bv[u][j]));
+#pragma unroll
+        for (int u = 0; u < KSC; ++u) ak[0][u] = *reinterpret_cast<const f16x8*>(sPK + c * Cfg::PK + 32 * u + 8 * g4);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          if (ft + 1 < FT) {
+#pragma unroll
+            for (int u = 0; u < KSC; ++u)
+              ak[(ft + 1) & 1][u] =
+                  *reinterpret_cast<const f16x8*>(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
+          }
 #pragma unroll
           for (int u = 0; u < KSC; ++u)
-            ak[(ft + 1) & 1][u] = lds_frag8(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
+            S[ft] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ft & 1][u], bvh[u], S[ft], 0, 0, 0);
         }
+      } else {
+        frag ak[2][KSC];
 #pragma unroll
-        for (int u = 0; u < KSC; ++u) S[ft] = M::step(ak[ft & 1][u], bv[u], S[ft]);
+        for (int u = 0; u < KSC; ++u) ak[0][u] = lds_frag8(sPK + c * Cfg::PK + 32 * u + 8 * g4);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          if (ft + 1 < FT) {
+#pragma unroll
+            for (int u = 0; u < KSC; ++u)
+              ak[(ft + 1) & 1][u] = lds_frag8(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
+          }
+#pragma unroll
+          for (int u = 0; u < KSC; ++u) S[ft] = M::step(ak[ft & 1][u], bv[u], S[ft]);
+        }
       }
     }
     __syncthreads();
@@ -827,10 +911,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int f = f0 + 16 * ft + 4 * g4 + i;
           if (f < Cfg::F) {
+            const float sc = state_scale<Cfg>(f);
             if (w < NW - 1)
-              a.S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = S[ft][i];
+              a.S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = sc * S[ft][i];
             else if (c == 0)
-              a.z[static_cast<size_t>(bh) * Cfg::F + f] = S[ft][i];
+              a.z[static_cast<size_t>(bh) * Cfg::F + f] = sc * S[ft][i];
           }
         }
     }
@@ -894,10 +979,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void state_store_kernel(const float* fin
     for (int i = 0; i < 4; ++i) {
       const int f = gsl * Cfg::FS + 16 * ft + 4 * g4 + i;
       if (f < Cfg::F) {
+        const float sc = state_scale<Cfg>(f);
         if (w < NW - 1)
-          S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = val[i];
+          S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = sc * val[i];
         else if (c == 0)
-          z[static_cast<size_t>(bh) * Cfg::F + f] = val[i];
+          z[static_cast<size_t>(bh) * Cfg::F + f] = sc * val[i];
       }
     }
   }
