@@ -38,16 +38,19 @@ CHUNK = 32                      # tokens per chunk of the order-2 d=16 bf16 kern
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic_based_order2_prefill.json")
 
 
+# sources the timed order-2 d=16 bf16 prefill kernel is compiled from
+TIMED_SOURCES = ("prefill_o2.hip", "internal.hpp", "mma.hpp")
+
+
 def source_hash():
-    """Hash of the HIP sources, to tell whether stored counter data still
-    describes the kernels being timed."""
+    """Hash of the timed kernel's HIP sources, to tell whether stored counter
+    data still describes the kernel being timed."""
     import hashlib
     csrc = os.path.join(ROOT, "taylor_series_linear_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in TIMED_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
