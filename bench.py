@@ -236,6 +236,96 @@ def bench_decode(args, torch, tl, W):
     }
 
 
+def _fit_exponent(ns, ts):
+    """Least-squares slope of log t against log N."""
+    x = np.log(np.asarray(ns, dtype=np.float64))
+    y = np.log(np.asarray(ts, dtype=np.float64))
+    return float(np.polyfit(x, y, 1)[0])
+
+
+def _unit_rows(shape, gen, torch):
+    x = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    return x / x.norm(dim=-1, keepdim=True)
+
+
+def sweep(args, torch, tl):
+    """Growth of prefill time with N and of decode step time with the context
+    length, at the defaults of "Expanding Attention" (d=16, dv=64, a=2,
+    order 2, unit-sphere queries and keys). Prints one JSON line per point and
+    one per fit; inputs are drawn on the device from a seeded generator."""
+    d, dv, n_terms, a = 16, 64, 3, 2.0
+    gen = torch.Generator(device="cuda")
+    L = tl.lib()
+    # prefill: 64 heads, N = 1024 .. 65536, fp32 and bf16 inputs
+    H = 64
+    ns = [1024 * 2 ** i for i in range(7)]
+    for dt in ("f32", "bf16"):
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        code = tl.TAYLOR_F32 if dt == "f32" else tl.TAYLOR_BF16
+        times = []
+        for N in ns:
+            gen.manual_seed(2000 + N)
+            q = _unit_rows((1, H, N, d), gen, torch).to(tdt)
+            k = _unit_rows((1, H, N, d), gen, torch).to(tdt)
+            v = torch.randn((1, H, N, dv), generator=gen, device="cuda").to(tdt)
+            o = torch.empty((1, H, N, dv), dtype=tdt, device="cuda")
+            wsb = tl.prefill_workspace_bytes(1, H, N, d, dv, n_terms, tdt)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+            def step(i):
+                st = L.taylor_attn_prefill(tl._ptr(q), tl._ptr(k), tl._ptr(v), code, 1, H, N, d, dv, n_terms, a,
+                                           None, None, tl._ptr(o), code, None, None, tl._ptr(ws), wsb,
+                                           tl._stream())
+                if st != 0:
+                    tl.check(st)
+
+            for i in range(3):
+                step(i)
+            ms = time_loop(step, 10, torch)
+            times.append(ms)
+            print(json.dumps({"sweep": "prefill", "dtype": dt, "heads": H, "N": N, "ms": ms,
+                              "token_heads_per_s": H * N / (ms * 1e-3)}), flush=True)
+            del q, k, v, o, ws
+        big = [i for i, N in enumerate(ns) if N >= 8192]
+        print(json.dumps({"sweep": "prefill_fit", "dtype": dt, "exponent_all": _fit_exponent(ns, times),
+                          "exponent_N_ge_8192": _fit_exponent([ns[i] for i in big], [times[i] for i in big]),
+                          "N": [ns[0], ns[-1]]}), flush=True)
+    # decode: 1024 heads (64 sequences x 16), fp32, after contexts of 1024 .. 65536 tokens
+    B, Hd, R, steps = 64, 16, 8, 256
+    ctx = [1024, 4096, 16384, 65536]
+    times = []
+    for N in ctx:
+        gen.manual_seed(3000 + N)
+        k = _unit_rows((B, Hd, N, d), gen, torch)
+        v = torch.randn((B, Hd, N, dv), generator=gen, device="cuda")
+        _, S, z = tl.prefill(k, k, v, n_terms, a, want_output=False, return_state=True)
+        del k, v
+        Ss = [S.clone() for _ in range(R)]
+        zs = [z.clone() for _ in range(R)]
+        sq = _unit_rows((steps, B, Hd, d), gen, torch)
+        sk = _unit_rows((steps, B, Hd, d), gen, torch)
+        sv = torch.randn((steps, B, Hd, dv), generator=gen, device="cuda")
+        o = torch.empty((B, Hd, dv), dtype=torch.float32, device="cuda")
+
+        def dstep(i):
+            s, r = i % steps, i % R
+            st = L.taylor_attn_decode(tl._ptr(sq[s]), tl._ptr(sk[s]), tl._ptr(sv[s]), tl.TAYLOR_F32, B, Hd, d, dv,
+                                      n_terms, a, tl._ptr(Ss[r]), tl._ptr(zs[r]), tl._ptr(o), tl.TAYLOR_F32,
+                                      tl._stream())
+            if st != 0:
+                tl.check(st)
+
+        for i in range(32):
+            dstep(i)
+        ms = time_loop(dstep, steps, torch)
+        times.append(ms)
+        print(json.dumps({"sweep": "decode", "dtype": "f32", "heads": B * Hd, "context": N,
+                          "us_per_step": ms * 1e3, "state_replicas": R}), flush=True)
+        del Ss, zs, S, z, sq, sk, sv
+    print(json.dumps({"sweep": "decode_fit", "exponent": _fit_exponent(ctx, times), "context": [ctx[0], ctx[-1]]}),
+          flush=True)
+
+
 def cpu_baseline(w, x, budget_s):
     """fp64 oracle direct() on the first heads of the same inputs until ~budget_s."""
     from oracle import taylor_oracle as T
@@ -270,6 +360,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--sweep", action="store_true",
+                    help="growth of prefill time with N and of decode time with the context, then exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise rocprofv3 --pmc runs into the stored traffic record and exit")
     args = ap.parse_args()
@@ -288,6 +380,9 @@ def main():
     import workloads as W
 
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(args, torch, tl)
+        return
     if args.only == "copy":
         # plain copy of known size, for counter calibration (FETCH_SIZE / WRITE_SIZE)
         n = 256 * 1024 * 1024 // 4

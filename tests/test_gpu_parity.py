@@ -251,3 +251,26 @@ def test_bf16_output_matches_fp32_output():
     o32 = _run_prefill(x, 3, 4.0, "bf16", out_dtype=torch.float32)
     o16 = _run_prefill(x, 3, 4.0, "bf16", out_dtype=torch.bfloat16)
     assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+
+
+def test_error_vs_softmax_decreases_with_order():
+    # "Expanding Attention", defaults paragraph and the order trade-off: at
+    # d=16, dv=64, a=2 with unit-sphere queries and keys, the deviation from
+    # causal softmax with the same a falls as terms are added. The kernels'
+    # own rounding must stay far below that truncation error, so the GPU
+    # error tracks the fp64 oracle's Taylor-vs-softmax error at every n.
+    B, H, N, d, dv, a = 1, 2, 1024, 16, 64, 2.0
+    x = _inputs(B, H, N, d, dv, "f32", 4242, qk="unit")
+    ref = np.stack([T.softmax_causal(x["q64"][0, h], x["k64"][0, h], x["v64"][0, h], a) for h in range(H)])[None]
+    errs = []
+    for n in (1, 3, 5):
+        say("error vs softmax, n =", n)
+        o = to_f64(_run_prefill(x, n, a, "f32"))
+        tay = T.direct(x["q64"], x["k64"], x["v64"], n, a)
+        e_gpu = float(np.max(np.abs(o - ref)))
+        e_ora = float(np.max(np.abs(tay - ref)))
+        say(f"  n={n}: max|o - softmax| GPU {e_gpu:.3e}, oracle {e_ora:.3e}; normwise GPU "
+            f"{normwise_rel(o, ref):.3e}")
+        assert abs(e_gpu - e_ora) < 1e-5 + 1e-2 * e_ora
+        errs.append(e_gpu)
+    assert errs[0] > errs[1] > errs[2]

@@ -393,6 +393,26 @@ def test_direct_batched_and_rows():
 # Accuracy against softmax (C-P11): the trend only; 6.5e-4 stays unpinned
 # ----------------------------------------------------------------------------
 
+def test_softmax_oracle_pins():
+    # The softmax reference pinned without its own formula: (1) the Taylor
+    # series converges to exp, so direct() with 30 terms equals it when
+    # |q.k/a| <= 1/2 (remainder below 1e-40); (2) equal keys give equal
+    # weights, i.e. the prefix mean of v; (3) one token returns its value.
+    rng = np.random.default_rng(23)
+    N, d, dv, a = 96, 16, 8, 2.0
+    q = rng.standard_normal((N, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, dv))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    ref = T.softmax_causal(q, k, v, a, block=40)
+    assert rel(ref, T.direct(q, k, v, 30, a)) < 1e-13
+    keq = np.repeat(k[:1], N, axis=0)
+    prefix_mean = np.cumsum(v, axis=0) / np.arange(1, N + 1)[:, None]
+    assert rel(T.softmax_causal(q, keq, v, a), prefix_mean) < 1e-14
+    assert rel(T.softmax_causal(q[:1], k[:1], v[:1], a), v[:1]) < 1e-15
+
+
 def test_error_vs_softmax_decreases_with_order():
     rng = np.random.default_rng(17)
     N, d, dv, a = 256, 16, 64, 2.0  # EA defaults, unit-sphere q and k

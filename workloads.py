@@ -8,7 +8,8 @@ holds none of the attention arithmetic. Recipe, for every workload:
 * Draw order inside a head: q [N, d], then k [N, d], then v [N, dv], as
   float64 standard normals.
 * ``qk="l2x2"``: every q and k row is scaled to Euclidean norm 2 in float64
-  before rounding (the order-4 workload).
+  before rounding (the order-4 workload); ``qk="unit"``: to norm 1 (the
+  unit-sphere defaults of the accuracy-against-softmax measurement).
 * Rounding: float64 -> float32 (round to nearest even) -> bf16 (round to
   nearest even on the fp32 bit pattern) when the storage type is bf16.
 
@@ -48,7 +49,7 @@ class Workload:
     a: float
     dtype: str          # "f32" or "bf16": storage type of q, k, v
     seed: int
-    qk: str = "normal"  # "normal" or "l2x2"
+    qk: str = "normal"  # "normal", "l2x2" or "unit"
     steps: int = 0      # decode steps after an N-token prefill (decode workload)
     notes: str = field(default="", compare=False)
 
@@ -108,9 +109,10 @@ def _head_draw(seed, b, h, N, d, dv, qk):
     q = rng.standard_normal((N, d))
     k = rng.standard_normal((N, d))
     v = rng.standard_normal((N, dv))
-    if qk == "l2x2":
-        q = 2.0 * q / np.linalg.norm(q, axis=1, keepdims=True)
-        k = 2.0 * k / np.linalg.norm(k, axis=1, keepdims=True)
+    if qk in ("l2x2", "unit"):
+        r = 2.0 if qk == "l2x2" else 1.0
+        q = r * q / np.linalg.norm(q, axis=1, keepdims=True)
+        k = r * k / np.linalg.norm(k, axis=1, keepdims=True)
     return q, k, v
 
 
