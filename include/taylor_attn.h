@@ -41,7 +41,7 @@
  *  - taylor_last_error() returns a message for the last non-OK status on the
  *    calling thread (thread-local; valid until the next call on that thread).
  *  - Supported (d, dv, n_terms): d = 16 with dv in {16, 64} and n_terms in
- *    {1, 3, 5}; d = 64 with dv in {16, 64} and n_terms in {1, 3}. n_terms must
+ *    {1, 3, 5}; d = 32 or 64 with dv in {16, 64} and n_terms in {1, 3}. n_terms must
  *    be odd so that the highest order is even and every weight is positive
  *    ("Two prerequisites" on the same page; posfloor README, "The 1/2
  *    positivity floor": even truncations are globally positive). Anything
@@ -124,11 +124,14 @@ size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_t
  * B, H or N may be 0: then no token is processed; with N = 0 the final state
  * is S0 (or zero). The normalisation divides by a sum of weights that is
  * >= 1/2 per key for n_terms = 3 (>= 0.27 for 5), so it never divides by 0.
- * Range: the bf16 order-2 d = 16 dv = 64 instantiation carries keys, values,
- * key products k_i k_j and the weights w(q.k/a) in fp16 inside its state
- * update and intra-chunk term (fp32 accumulation), so |k_i k_j|, |v| and
- * w(q.k/a) must stay below 65504; under the normalisation the method asks for
- * (|q.k/a| of order 1) this always holds.
+ * Range: several bf16 instantiations carry key-side products in fp16 inside
+ * the state update (fp32 accumulation): order 2 with d = 16 and dv = 64 (keys,
+ * values, k_i k_j and the weights w(q.k/a), also in its intra-chunk term) and
+ * d = 64 (k_i k_j and values) need those below 65504; the other bf16
+ * instantiations with n_terms > 1 and d > 16 or n_terms = 5 use keys halved,
+ * so the products of m halved coordinates (m <= 4) must stay below 65504,
+ * e.g. |k_i| < 32 for n_terms = 5. Under the normalisation the method asks
+ * for (|q.k/a| of order 1) these always hold.
  */
 taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   taylor_dtype in_dtype, int B, int H, int N, int d, int dv,

@@ -21,7 +21,7 @@ taylor_status fail(taylor_status s, const std::string& msg) {
 bool supported(int d, int dv, int n_terms) {
   if (dv != 16 && dv != 64) return false;
   if (d == 16) return n_terms == 1 || n_terms == 3 || n_terms == 5;
-  if (d == 64) return n_terms == 1 || n_terms == 3;
+  if (d == 32 || d == 64) return n_terms == 1 || n_terms == 3;
   return false;
 }
 
@@ -37,7 +37,7 @@ taylor_status check_dn(int d, int dv, int n_terms, bool with_dv) {
                 "unsupported configuration d=" + std::to_string(d) +
                     (with_dv ? " dv=" + std::to_string(dv) : std::string()) +
                     " n_terms=" + std::to_string(n_terms) +
-                    " (supported: d=16 with n_terms 1,3,5; d=64 with n_terms 1,3; dv 16 or 64)");
+                    " (supported: d=16 with n_terms 1,3,5; d=32 or 64 with n_terms 1,3; dv 16 or 64)");
   return TAYLOR_OK;
 }
 

@@ -172,6 +172,10 @@ __global__ __launch_bounds__(256) void feature_map_kernel(const void* x, int64_t
   X(16, 64, 3)            \
   X(16, 16, 5)            \
   X(16, 64, 5)            \
+  X(32, 16, 1)            \
+  X(32, 64, 1)            \
+  X(32, 16, 3)            \
+  X(32, 64, 3)            \
   X(64, 16, 1)            \
   X(64, 64, 1)            \
   X(64, 16, 3)            \
@@ -207,7 +211,7 @@ hipError_t feature_map_launch(int d, int n_terms, bool bf16, const void* x, int6
                          x, rows, phi, sc);                                                       \
     return hipGetLastError();                                                                     \
   }
-  X(16, 1) X(16, 3) X(16, 5) X(64, 1) X(64, 3)
+  X(16, 1) X(16, 3) X(16, 5) X(32, 1) X(32, 3) X(64, 1) X(64, 3)
 #undef X
   return hipErrorInvalidValue;
 }

@@ -1037,6 +1037,14 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(16, 16, 5, false, 256, 32, false)       \
   X(16, 64, 5, true, 608, 32, false)        \
   X(16, 64, 5, false, 256, 32, false)       \
+  X(32, 16, 1, true, 32, 64, true)          \
+  X(32, 16, 1, false, 32, 64, true)         \
+  X(32, 64, 1, true, 32, 64, true)          \
+  X(32, 64, 1, false, 32, 64, true)         \
+  X(32, 16, 3, true, 576, 32, false)        \
+  X(32, 16, 3, false, 128, 32, false)       \
+  X(32, 64, 3, true, 288, 32, false)        \
+  X(32, 64, 3, false, 128, 32, false)       \
   X(64, 16, 1, true, 32, 64, true)          \
   X(64, 16, 1, false, 32, 64, true)         \
   X(64, 64, 1, true, 32, 64, true)          \

@@ -31,7 +31,8 @@ def test_feature_dim():
 
 
 def test_supported_set():
-    ok = {(16, dv, n) for dv in (16, 64) for n in (1, 3, 5)} | {(64, dv, n) for dv in (16, 64) for n in (1, 3)}
+    ok = {(16, dv, n) for dv in (16, 64) for n in (1, 3, 5)} | {(dd, dv, n) for dd in (32, 64) for dv in (16, 64)
+                                                                for n in (1, 3)}
     for d in (8, 16, 32, 64):
         for dv in (8, 16, 32, 64, 128):
             for n in range(0, 7):
@@ -53,7 +54,8 @@ def test_prefill_rejects_bad_arguments():
     assert _prefill(n=2) == TAYLOR_ERR_UNSUPPORTED
     assert b"odd" in L.taylor_last_error()
     assert _prefill(n=4) == TAYLOR_ERR_UNSUPPORTED
-    assert _prefill(d=32) == TAYLOR_ERR_UNSUPPORTED
+    assert _prefill(d=48) == TAYLOR_ERR_UNSUPPORTED
+    assert _prefill(d=32, n=5) == TAYLOR_ERR_UNSUPPORTED
     assert _prefill(dv=32) == TAYLOR_ERR_UNSUPPORTED
     assert _prefill(d=64, n=5) == TAYLOR_ERR_UNSUPPORTED
     assert _prefill(in_dtype=7) == TAYLOR_ERR_UNSUPPORTED

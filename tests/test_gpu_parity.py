@@ -23,6 +23,7 @@ import taylor_series_linear_amd as tl  # noqa: E402
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 CONFIGS = [(16, 16, 1), (16, 64, 1), (16, 16, 3), (16, 64, 3), (16, 16, 5), (16, 64, 5),
+           (32, 16, 1), (32, 64, 1), (32, 16, 3), (32, 64, 3),
            (64, 16, 1), (64, 64, 1), (64, 16, 3), (64, 64, 3)]
 
 
@@ -49,7 +50,7 @@ def _qk_kind(d, n):
     return "l2x2" if n == 5 else "normal"
 
 
-@pytest.mark.parametrize("d,n", [(16, 1), (16, 3), (16, 5), (64, 1), (64, 3)])
+@pytest.mark.parametrize("d,n", [(16, 1), (16, 3), (16, 5), (32, 1), (32, 3), (64, 1), (64, 3)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("fold", [False, True])
 def test_feature_map(d, n, dtype, fold):
@@ -86,7 +87,7 @@ def test_prefill_small(d, dv, n, dtype, N):
     assert normwise_rel(to_f64(z)[..., None], zr[..., None]) < TOL[dtype]
 
 
-@pytest.mark.parametrize("d,dv,n", [(16, 64, 3), (16, 16, 1), (64, 64, 3), (16, 64, 5)])
+@pytest.mark.parametrize("d,dv,n", [(16, 64, 3), (16, 16, 1), (32, 64, 3), (64, 64, 3), (16, 64, 5)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_multi_segment(d, dv, n, dtype):
     # long enough that the sequence is split into several segments
@@ -274,3 +275,24 @@ def test_error_vs_softmax_decreases_with_order():
         assert abs(e_gpu - e_ora) < 1e-5 + 1e-2 * e_ora
         errs.append(e_gpu)
     assert errs[0] > errs[1] > errs[2]
+
+
+@pytest.mark.parametrize("d,n", [(16, 3), (32, 3), (16, 5)])
+def test_state_rank_on_gpu_features(d, n):
+    # "Expanding Attention", "Higher orders": the order-m block of phi has
+    # C(d+m-1, m) independent columns, so for N >= F_m generic keys the
+    # feature matrix built by the GPU feature map has exactly that rank
+    # (singular values cut at 1e-4 of the largest, fp32 features).
+    N = 2 * T.n_features(d, n)
+    x = _inputs(1, 1, N, d, 4, "f32", 808, qk="unit")
+    phi = to_f64(tl.feature_map(to_device(x["k"], "f32")[0, 0], n))
+    torch.cuda.synchronize()
+    f0 = 0
+    for m in range(n):
+        Fm = math.comb(d + m - 1, m)
+        s = np.linalg.svd(phi[:, f0:f0 + Fm], compute_uv=False)
+        rank = int(np.sum(s > 1e-4 * s[0]))
+        say(f"d={d} order {m}: rank {rank} of {Fm}")
+        assert rank == Fm
+        f0 += Fm
+    assert f0 == phi.shape[1]
