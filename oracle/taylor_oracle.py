@@ -21,7 +21,9 @@ and visibly, in float64 (or exact ``fractions.Fraction``):
   law and the end-to-end weight check ("The sqrt(N) selectivity tax").
 * The Spanish linear-attention explainer (called LA below): the recurrence
   S_t = S_{t-1} + v_t phi(k_t)^T, o_t = S_t phi(q_t) -- update first, then
-  read out.
+  read out; and, in its paragraph on superposed memory, forgetting by a decay
+  that multiplies S_{t-1} before the write (the Mamba-2 reading of linear
+  attention with decay).
 
 Readings taken where the pages leave a step open:
 * n_terms counts Taylor terms m = 0 .. n-1; "order k" means n = k + 1.
@@ -31,6 +33,11 @@ Readings taken where the pages leave a step open:
   applied at read-out (or folded into phi(q) when ``a`` is passed to phi).
 * Canonical feature order: m ascending; within an order, non-decreasing
   index tuples in lexicographic order.
+* Decay (``gamma``): one constant factor gamma in (0, 1] for every step,
+  applied to S and z alike (z is the state of the all-ones value column), so
+  the output stays a normalised average: token s enters the output at time
+  t >= s with weight gamma^(t-s) w_ts, and an initial state S0/z0 (the state
+  just before token 0) with gamma^(t+1). gamma = 1 is the plain method.
 """
 from __future__ import annotations
 
@@ -138,7 +145,7 @@ def alpha_vector(d: int, n_terms: int, a: float) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def direct(q, k, v, n_terms: int, a: float, S0=None, z0=None,
-           rows=None, block: int = 256) -> np.ndarray:
+           rows=None, block: int = 256, gamma: float = 1.0) -> np.ndarray:
     """Causal normalised polynomial-weighted average, O(N^2), float64.
 
     For one head (q, k: N x d, v: N x dv):
@@ -150,6 +157,8 @@ def direct(q, k, v, n_terms: int, a: float, S0=None, z0=None,
 
     Leading batch axes are allowed: q[..., N, d]. ``rows`` restricts the
     output to the given query positions (the result is then [..., len(rows), dv]).
+    With a decay gamma < 1 every weight w_ts is multiplied by gamma^(t-s) and
+    the initial-state terms by gamma^(t+1) (module notes).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -160,7 +169,7 @@ def direct(q, k, v, n_terms: int, a: float, S0=None, z0=None,
         for idx in np.ndindex(*lead):
             s0 = None if S0 is None else np.asarray(S0)[idx]
             zz = None if z0 is None else np.asarray(z0)[idx]
-            o = direct(q[idx], k[idx], v[idx], n_terms, a, s0, zz, rows, block)
+            o = direct(q[idx], k[idx], v[idx], n_terms, a, s0, zz, rows, block, gamma)
             if out is None:
                 out = np.empty(lead + o.shape, dtype=np.float64)
             out[idx] = o
@@ -174,12 +183,16 @@ def direct(q, k, v, n_terms: int, a: float, S0=None, z0=None,
         T = (q[r] @ k[:e].T) / a
         W = taylor_weight(T, n_terms)
         W = np.where(np.arange(e)[None, :] <= r[:, None], W, 0.0)
+        if gamma != 1.0:
+            lag = np.maximum(r[:, None] - np.arange(e)[None, :], 0).astype(np.float64)
+            W = W * np.power(float(gamma), lag)
         num = W @ v[:e]
         den = W.sum(axis=1)
         if S0 is not None:
             fq = phi(q[r], n_terms) * alpha_vector(q.shape[1], n_terms, a)
-            num = num + fq @ np.asarray(S0, dtype=np.float64)
-            den = den + fq @ np.asarray(z0, dtype=np.float64)
+            carry = np.power(float(gamma), r + 1.0) if gamma != 1.0 else np.ones(len(r))
+            num = num + carry[:, None] * (fq @ np.asarray(S0, dtype=np.float64))
+            den = den + carry * (fq @ np.asarray(z0, dtype=np.float64))
         out[b0:b0 + len(r)] = num / den[:, None]
     return out
 
@@ -188,9 +201,10 @@ def direct(q, k, v, n_terms: int, a: float, S0=None, z0=None,
 # States (EA "Memory"; LA recurrence)
 # --------------------------------------------------------------------------
 
-def state(k, v, n_terms: int, S0=None, z0=None):
+def state(k, v, n_terms: int, S0=None, z0=None, gamma: float = 1.0):
     """Per-order states after the given tokens: S = S0 + phi(K)^T V, z = z0 + phi(K)^T 1.
 
+    With a decay, token s of N enters with gamma^(N-1-s) and S0, z0 with gamma^N.
     Shapes: k [..., N, d], v [..., N, dv] -> S [..., F, dv], z [..., F].
     """
     k = np.asarray(k, dtype=np.float64)
@@ -203,21 +217,24 @@ def state(k, v, n_terms: int, S0=None, z0=None):
         for idx in np.ndindex(*lead):
             S[idx], z[idx] = state(k[idx], v[idx], n_terms,
                                    None if S0 is None else np.asarray(S0)[idx],
-                                   None if z0 is None else np.asarray(z0)[idx])
+                                   None if z0 is None else np.asarray(z0)[idx], gamma)
         return S, z
     fk = phi(k, n_terms)
-    S = fk.T @ v
-    z = fk.sum(axis=0)
+    N = k.shape[0]
+    dec = np.power(float(gamma), np.arange(N - 1, -1, -1, dtype=np.float64)) if gamma != 1.0 else np.ones(N)
+    S = (fk * dec[:, None]).T @ v
+    z = fk.T @ dec
     if S0 is not None:
-        S = S + np.asarray(S0, dtype=np.float64)
-        z = z + np.asarray(z0, dtype=np.float64)
+        carry = float(gamma) ** N if gamma != 1.0 else 1.0
+        S = S + carry * np.asarray(S0, dtype=np.float64)
+        z = z + carry * np.asarray(z0, dtype=np.float64)
     return S, z
 
 
-def recurrent(q, k, v, n_terms: int, a: float, S0=None, z0=None):
+def recurrent(q, k, v, n_terms: int, a: float, S0=None, z0=None, gamma: float = 1.0):
     """Token-by-token recurrence for one head (LA: update, then read out).
 
-    S_t = S_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t),
+    S_t = gamma S_{t-1} + phi(k_t) v_t^T,  z_t = gamma z_{t-1} + phi(k_t),
     o_t = sum_m alpha_m phi_m(q_t).S_m,t / sum_m alpha_m phi_m(q_t).z_m,t.
     Returns (o [N, dv], S [F, dv], z [F]).
     """
@@ -232,21 +249,21 @@ def recurrent(q, k, v, n_terms: int, a: float, S0=None, z0=None):
     out = np.empty((N, v.shape[1]))
     for t in range(N):
         fk = phi(k[t:t + 1], n_terms)[0]
-        S = S + np.outer(fk, v[t])
-        z = z + fk
+        S = gamma * S + np.outer(fk, v[t])
+        z = gamma * z + fk
         fq = phi(q[t:t + 1], n_terms)[0] * alpha
         out[t] = (fq @ S) / (fq @ z)
     return out, S, z
 
 
-def decode_step(q, k, v, S, z, n_terms: int, a: float):
-    """One generation step for one head: update with (k, v), then read out with q.
+def decode_step(q, k, v, S, z, n_terms: int, a: float, gamma: float = 1.0):
+    """One generation step for one head: decay, update with (k, v), then read out with q.
 
     Returns (o [dv], S_new [F, dv], z_new [F]).
     """
     fk = phi(np.asarray(k, dtype=np.float64)[None, :], n_terms)[0]
-    S_new = np.asarray(S, dtype=np.float64) + np.outer(fk, np.asarray(v, dtype=np.float64))
-    z_new = np.asarray(z, dtype=np.float64) + fk
+    S_new = gamma * np.asarray(S, dtype=np.float64) + np.outer(fk, np.asarray(v, dtype=np.float64))
+    z_new = gamma * np.asarray(z, dtype=np.float64) + fk
     d = len(q)
     fq = phi(np.asarray(q, dtype=np.float64)[None, :], n_terms)[0] * alpha_vector(d, n_terms, a)
     return (fq @ S_new) / (fq @ z_new), S_new, z_new

@@ -425,3 +425,57 @@ def test_error_vs_softmax_decreases_with_order():
     errs = [np.max(np.abs(T.direct(q, k, v, n, a) - ref)) for n in (1, 2, 3, 4, 5)]
     assert all(e1 > e2 for e1, e2 in zip(errs, errs[1:]))
     assert errs[2] < 1e-2  # order 2 already close, consistent in size with EA's 6.5e-4
+
+
+# ----------------------------------------------------------------------------
+# Decayed state (LA, superposed-memory paragraph: a decay multiplying S_{t-1})
+# ----------------------------------------------------------------------------
+
+def test_decay_geometric_closed_form():
+    # n = 1 (every weight 1) and scalar values v_s = r^s: the decayed average
+    # is a ratio of two geometric sums,
+    #   o_t = [(r^(t+1) - g^(t+1)) / (r - g)] * [(1 - g) / (1 - g^(t+1))].
+    N, g, r = 40, 0.9, 1.03
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((N, 4))
+    k = rng.standard_normal((N, 4))
+    v = (r ** np.arange(N, dtype=np.float64))[:, None]
+    t = np.arange(N, dtype=np.float64)
+    want = (r ** (t + 1) - g ** (t + 1)) / (r - g) * (1 - g) / (1 - g ** (t + 1))
+    assert rel(T.direct(q, k, v, 1, 1.0, gamma=g)[:, 0], want) < 1e-14
+    assert rel(T.recurrent(q, k, v, 1, 1.0, gamma=g)[0][:, 0], want) < 1e-13
+
+
+def test_decay_recurrent_equals_direct_and_limits():
+    rng = np.random.default_rng(6)
+    N, d, dv, a = 48, 4, 3, 2.0
+    q = rng.standard_normal((N, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, dv))
+    for n in (1, 3, 5):
+        for g in (0.5, 0.97):
+            o_dir = T.direct(q, k, v, n, a, gamma=g)
+            o_rec, S, z = T.recurrent(q, k, v, n, a, gamma=g)
+            assert rel(o_rec, o_dir) < 1e-12
+            S2, z2 = T.state(k, v, n, gamma=g)
+            assert rel(S, S2) < 1e-12 and rel(z, z2) < 1e-12
+    # gamma = 1 is the plain method; a vanishing gamma keeps only the
+    # current token, o_t = v_t
+    assert rel(T.direct(q, k, v, 3, a, gamma=1.0), T.direct(q, k, v, 3, a)) == 0
+    assert rel(T.direct(q, k, v, 3, a, gamma=1e-30), v) < 1e-15
+
+
+def test_decay_continuation_through_state():
+    # the state after the first part, decayed, carries it exactly: direct on
+    # the second part from S0 = state(first part) equals the whole sequence
+    rng = np.random.default_rng(7)
+    N1, N2, d, dv, a, g = 30, 25, 4, 3, 2.0, 0.93
+    q = rng.standard_normal((N1 + N2, d))
+    k = rng.standard_normal((N1 + N2, d))
+    v = rng.standard_normal((N1 + N2, dv))
+    S0, z0 = T.state(k[:N1], v[:N1], 3, gamma=g)
+    part = T.direct(q[N1:], k[N1:], v[N1:], 3, a, S0, z0, gamma=g)
+    whole = T.direct(q, k, v, 3, a, gamma=g)[N1:]
+    assert rel(part, whole) < 1e-13
+    o, S, z = T.decode_step(q[N1], k[N1], v[N1], S0, z0, 3, a, gamma=g)
+    assert rel(o, whole[0]) < 1e-13
