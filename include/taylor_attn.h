@@ -153,6 +153,35 @@ taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
                                  int n_terms, float a, float* S, float* z, void* o,
                                  taylor_dtype out_dtype, void* stream);
 
+/*
+ * Decayed state (Spanish linear-attention explainer, paragraph on the
+ * superposed memory: forgetting by a decay that multiplies S_{t-1} before
+ * each write, the reading of Mamba-2 as linear attention with decay). One
+ * constant gamma for every step, head and order, applied to S and z alike:
+ *   S_t = gamma S_{t-1} + phi(k_t) v_t^T,  z_t = gamma z_{t-1} + phi(k_t),
+ *   o_t = sum_m alpha_m phi_m(q_t).S_m,t / sum_m alpha_m phi_m(q_t).z_m,t,
+ * i.e. token s enters o_t with weight gamma^(t-s) w(q_t.k_s/a), and S0/z0
+ * (the state just before token 0) with gamma^(t+1). gamma = 1 gives the
+ * plain results (up to rounding; the decayed prefill always runs the generic
+ * kernel family).
+ * Arguments, layouts, ownership and errors are those of taylor_attn_prefill
+ * and taylor_attn_decode, plus:
+ *   gamma  0 < gamma <= 1 and finite, else TAYLOR_ERR_BAD_SCALE.
+ * The workspace of the decayed prefill is sized by
+ * taylor_attn_prefill_decayed_workspace (independent of gamma).
+ */
+size_t taylor_attn_prefill_decayed_workspace(int B, int H, int N, int d, int dv, int n_terms,
+                                             taylor_dtype in_dtype);
+taylor_status taylor_attn_prefill_decayed(const void* q, const void* k, const void* v,
+                                          taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                          int n_terms, float a, float gamma, const float* S0,
+                                          const float* z0, void* o, taylor_dtype out_dtype, float* S,
+                                          float* z, void* workspace, size_t ws_bytes, void* stream);
+taylor_status taylor_attn_decode_decayed(const void* q, const void* k, const void* v,
+                                         taylor_dtype in_dtype, int B, int H, int d, int dv,
+                                         int n_terms, float a, float gamma, float* S, float* z, void* o,
+                                         taylor_dtype out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,14 @@ def lib() -> ctypes.CDLL:
     L.taylor_attn_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                      vp, vp, vp, i32, vp]
     L.taylor_attn_decode.restype = i32
+    L.taylor_attn_prefill_decayed_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.taylor_attn_prefill_decayed_workspace.restype = sz
+    L.taylor_attn_prefill_decayed.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
+                                              vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.taylor_attn_prefill_decayed.restype = i32
+    L.taylor_attn_decode_decayed.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
+                                             vp, vp, vp, i32, vp]
+    L.taylor_attn_decode_decayed.restype = i32
     del fp
     _lib = L
     return L
@@ -147,9 +155,10 @@ def feature_map(x, n_terms: int, a: float | None = None):
     return phi
 
 
-def prefill_workspace_bytes(B, H, N, d, dv, n_terms, in_dtype) -> int:
+def prefill_workspace_bytes(B, H, N, d, dv, n_terms, in_dtype, decayed: bool = False) -> int:
     code = TAYLOR_BF16 if str(in_dtype).endswith("bfloat16") or in_dtype == TAYLOR_BF16 else TAYLOR_F32
-    r = lib().taylor_attn_prefill_workspace(B, H, N, d, dv, n_terms, code)
+    fn = lib().taylor_attn_prefill_decayed_workspace if decayed else lib().taylor_attn_prefill_workspace
+    r = fn(B, H, N, d, dv, n_terms, code)
     if r == ctypes.c_size_t(-1).value:
         raise ValueError(lib().taylor_last_error().decode())
     return int(r)
@@ -157,12 +166,14 @@ def prefill_workspace_bytes(B, H, N, d, dv, n_terms, in_dtype) -> int:
 
 def prefill(q, k, v, n_terms: int, a: float, S0=None, z0=None, *, out_dtype=None,
             want_output: bool = True, return_state: bool = False, S=None, z=None,
-            workspace=None):
+            workspace=None, gamma: float | None = None):
     """Causal prefill. q, k [B, H, N, d], v [B, H, N, dv] (float32 or bfloat16, same dtype).
 
     Returns o [B, H, N, dv] (out_dtype, default q.dtype) or None, and with
     return_state=True also the final state (S [B, H, F, dv], z [B, H, F], float32).
     S / z may be passed to write the state into given buffers (they may be S0 / z0).
+    With ``gamma`` (0 < gamma <= 1) the state decays by gamma before every
+    write (taylor_attn_prefill_decayed).
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -184,21 +195,28 @@ def prefill(q, k, v, n_terms: int, a: float, S0=None, z0=None, *, out_dtype=None
             _need(t, n)
             if t.dtype != torch.float32:
                 raise ValueError(f"{n} must be float32")
-    ws_bytes = prefill_workspace_bytes(B, H, N, d, dv, n_terms, q.dtype)
+    ws_bytes = prefill_workspace_bytes(B, H, N, d, dv, n_terms, q.dtype, decayed=gamma is not None)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    check(lib().taylor_attn_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, dv, n_terms, float(a),
-        _ptr(S0), _ptr(z0), _ptr(o), TAYLOR_F32 if o is None else _dt(o), _ptr(S), _ptr(z),
-        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream()))
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    od = TAYLOR_F32 if o is None else _dt(o)
+    if gamma is None:
+        check(lib().taylor_attn_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, dv, n_terms, float(a),
+            _ptr(S0), _ptr(z0), _ptr(o), od, _ptr(S), _ptr(z), _ptr(workspace), ws_len, _stream()))
+    else:
+        check(lib().taylor_attn_prefill_decayed(
+            _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, dv, n_terms, float(a), float(gamma),
+            _ptr(S0), _ptr(z0), _ptr(o), od, _ptr(S), _ptr(z), _ptr(workspace), ws_len, _stream()))
     if return_state or S is not None:
         return o, S, z
     return o
 
 
-def decode(q, k, v, S, z, n_terms: int, a: float, *, out_dtype=None, o=None):
-    """One decode step: q, k [B, H, d], v [B, H, dv]; S, z updated in place. Returns o [B, H, dv]."""
+def decode(q, k, v, S, z, n_terms: int, a: float, *, out_dtype=None, o=None, gamma: float | None = None):
+    """One decode step: q, k [B, H, d], v [B, H, dv]; S, z updated in place. Returns o [B, H, dv].
+
+    With ``gamma`` the state decays by gamma before the write (taylor_attn_decode_decayed)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (S, "S"), (z, "z")):
         _need(t, n)
@@ -206,6 +224,11 @@ def decode(q, k, v, S, z, n_terms: int, a: float, *, out_dtype=None, o=None):
     dv = v.shape[-1]
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
-    check(lib().taylor_attn_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, d, dv, n_terms,
-                                   float(a), _ptr(S), _ptr(z), _ptr(o), _dt(o), _stream()))
+    if gamma is None:
+        check(lib().taylor_attn_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, d, dv, n_terms,
+                                       float(a), _ptr(S), _ptr(z), _ptr(o), _dt(o), _stream()))
+    else:
+        check(lib().taylor_attn_decode_decayed(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, d, dv, n_terms,
+                                               float(a), float(gamma), _ptr(S), _ptr(z), _ptr(o), _dt(o),
+                                               _stream()))
     return o

@@ -47,6 +47,12 @@ taylor_status check_scale(float a) {
   return TAYLOR_OK;
 }
 
+taylor_status check_gamma(float g) {
+  if (!std::isfinite(g) || !(g > 0.f) || g > 1.f)
+    return fail(TAYLOR_ERR_BAD_SCALE, "decay gamma must satisfy 0 < gamma <= 1");
+  return TAYLOR_OK;
+}
+
 taylor_status check_dtype(taylor_dtype t, const char* what) {
   if (t != TAYLOR_F32 && t != TAYLOR_BF16)
     return fail(TAYLOR_ERR_UNSUPPORTED, std::string(what) + " must be TAYLOR_F32 or TAYLOR_BF16");
@@ -71,7 +77,7 @@ taylor_status hip_status(hipError_t e, const char* where) {
 
 // Validation shared by the size query and the call; fills the plan.
 taylor_status check_prefill_shape(int B, int H, int N, int d, int dv, int n_terms,
-                                  taylor_dtype in_dtype, tl::PrefillPlan* plan) {
+                                  taylor_dtype in_dtype, bool decay, tl::PrefillPlan* plan) {
   taylor_status s = check_dtype(in_dtype, "in_dtype");
   if (s != TAYLOR_OK) return s;
   if (B < 0 || H < 0 || N < 0)
@@ -79,7 +85,7 @@ taylor_status check_prefill_shape(int B, int H, int N, int d, int dv, int n_term
   if ((s = check_dn(d, dv, n_terms, true)) != TAYLOR_OK) return s;
   if (checked_mul({B, H, N, d > dv ? d : dv}) < 0 || checked_mul({B, H}) > INT32_MAX / 64)
     return fail(TAYLOR_ERR_BAD_SHAPE, "B*H*N*max(d,dv) overflows");
-  if (!tl::prefill_plan(d, dv, n_terms, in_dtype == TAYLOR_BF16, B * H, N, plan))
+  if (!tl::prefill_plan(d, dv, n_terms, in_dtype == TAYLOR_BF16, decay, B * H, N, plan))
     return fail(TAYLOR_ERR_UNSUPPORTED, "no prefill instantiation for this configuration");
   return TAYLOR_OK;
 }
@@ -132,23 +138,23 @@ taylor_status taylor_feature_map(const void* x, taylor_dtype x_dtype, int64_t ro
                     "taylor_feature_map launch");
 }
 
-size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_terms,
-                                     taylor_dtype in_dtype) {
-  tl::PrefillPlan p;
-  if (check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &p) != TAYLOR_OK) return static_cast<size_t>(-1);
-  return p.bytes;
-}
+}  // extern "C"
 
-taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
-                                  taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
-                                  int n_terms, float a, const float* S0, const float* z0,
-                                  void* o, taylor_dtype out_dtype, float* S, float* z,
-                                  void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// Shared by the plain and the decayed prefill; `decay` selects the kernel
+// family (the decayed one also runs gamma = 1, so its workspace size does not
+// depend on gamma).
+taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B, int H,
+                           int N, int d, int dv, int n_terms, float a, bool decay, float gamma, const float* S0,
+                           const float* z0, void* o, taylor_dtype out_dtype, float* S, float* z,
+                           void* workspace, size_t ws_bytes, void* stream) {
   tl::PrefillPlan p;
-  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, &p);
+  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, decay, &p);
   if (s != TAYLOR_OK) return s;
   if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
   if ((s = check_scale(a)) != TAYLOR_OK) return s;
+  if (decay && (s = check_gamma(gamma)) != TAYLOR_OK) return s;
   if ((S0 == nullptr) != (z0 == nullptr))
     return fail(TAYLOR_ERR_NULL_PTR, "S0 and z0 must both be given or both be NULL");
   if ((S == nullptr) != (z == nullptr))
@@ -191,20 +197,22 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
   // while the last one finishes the state, so the final state goes through
   // the workspace and is copied out afterwards.
   args.defer_state = (S != nullptr && p.P > 1 && (S == S0 || z == z0)) ? 1 : 0;
+  args.decay = decay ? 1 : 0;
+  args.log2g = decay ? std::log2(gamma) : 0.f;
   return hip_status(tl::prefill_launch(d, dv, n_terms, in_dtype == TAYLOR_BF16, args, st),
                     "taylor_attn_prefill launch");
 }
 
-taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
-                                 taylor_dtype in_dtype, int B, int H, int d, int dv,
-                                 int n_terms, float a, float* S, float* z, void* o,
-                                 taylor_dtype out_dtype, void* stream) {
+taylor_status decode_impl(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B, int H,
+                          int d, int dv, int n_terms, float a, float gamma, float* S, float* z, void* o,
+                          taylor_dtype out_dtype, void* stream) {
   taylor_status s = check_dtype(in_dtype, "in_dtype");
   if (s != TAYLOR_OK) return s;
   if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
   if (B < 0 || H < 0) return fail(TAYLOR_ERR_BAD_SHAPE, "B and H must be >= 0");
   if ((s = check_dn(d, dv, n_terms, true)) != TAYLOR_OK) return s;
   if ((s = check_scale(a)) != TAYLOR_OK) return s;
+  if ((s = check_gamma(gamma)) != TAYLOR_OK) return s;
   if (checked_mul({B, H}) > INT32_MAX)
     return fail(TAYLOR_ERR_BAD_SHAPE, "B*H exceeds the grid limit");
   const int BH = B * H;
@@ -221,10 +229,63 @@ taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
   args.out_bf16 = out_dtype == TAYLOR_BF16;
   args.BH = BH;
   args.inv_a = 1.0f / a;
+  args.gamma = gamma;
   (void)hipGetLastError();
   return hip_status(tl::decode_launch(d, dv, n_terms, in_dtype == TAYLOR_BF16, args,
                                       static_cast<hipStream_t>(stream)),
                     "taylor_attn_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_terms,
+                                     taylor_dtype in_dtype) {
+  tl::PrefillPlan p;
+  if (check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, false, &p) != TAYLOR_OK)
+    return static_cast<size_t>(-1);
+  return p.bytes;
+}
+
+taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
+                                  taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                  int n_terms, float a, const float* S0, const float* z0,
+                                  void* o, taylor_dtype out_dtype, float* S, float* z,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, false, 1.f, S0, z0, o, out_dtype, S, z,
+                      workspace, ws_bytes, stream);
+}
+
+size_t taylor_attn_prefill_decayed_workspace(int B, int H, int N, int d, int dv, int n_terms,
+                                             taylor_dtype in_dtype) {
+  tl::PrefillPlan p;
+  if (check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, true, &p) != TAYLOR_OK)
+    return static_cast<size_t>(-1);
+  return p.bytes;
+}
+
+taylor_status taylor_attn_prefill_decayed(const void* q, const void* k, const void* v,
+                                          taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                          int n_terms, float a, float gamma, const float* S0,
+                                          const float* z0, void* o, taylor_dtype out_dtype, float* S,
+                                          float* z, void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, true, gamma, S0, z0, o, out_dtype, S, z,
+                      workspace, ws_bytes, stream);
+}
+
+taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
+                                 taylor_dtype in_dtype, int B, int H, int d, int dv,
+                                 int n_terms, float a, float* S, float* z, void* o,
+                                 taylor_dtype out_dtype, void* stream) {
+  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, 1.f, S, z, o, out_dtype, stream);
+}
+
+taylor_status taylor_attn_decode_decayed(const void* q, const void* k, const void* v,
+                                         taylor_dtype in_dtype, int B, int H, int d, int dv,
+                                         int n_terms, float a, float gamma, float* S, float* z, void* o,
+                                         taylor_dtype out_dtype, void* stream) {
+  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, gamma, S, z, o, out_dtype, stream);
 }
 
 }  // extern "C"

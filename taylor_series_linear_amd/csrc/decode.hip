@@ -3,10 +3,12 @@
 // Decode ("Expanding Attention: A Taylor-Series Route to Linear-Time
 // Transformers with a Fixed Number of Recurrent States", "Decoding": one
 // token costs sum_m C(d+m-1,m)(dv+1), independent of the context length):
-//   S_m += phi_m(k) v^T,  z_m += phi_m(k)      (update first ...)
+//   S_m = g S_m + phi_m(k) v^T,  z_m = g z_m + phi_m(k)      (update first ...)
 //   o = sum_m alpha_m phi_m(q)^T S_m / sum_m alpha_m phi_m(q)^T z_m  (... then read out)
 // following the linear-attention recurrence S_t = S_{t-1} + v_t phi(k_t)^T,
-// o_t = S_t phi(q_t) (Spanish linear-attention explainer).
+// o_t = S_t phi(q_t) (Spanish linear-attention explainer); g is the constant
+// decay that the same explainer's superposed-memory paragraph applies to
+// S_{t-1} before the write (g = 1: none).
 //
 // The step streams each head's state once: read, add, write back, and fold
 // the new row into the read-out while it is still in registers. It is bound
@@ -50,6 +52,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
   const float inv_a = a.inv_a;
+  const float g = a.gamma;
   const int dq = tid % NQ;
   const int rg = tid / NQ;
   float* Sh = a.S + static_cast<size_t>(bh) * F * DV;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     for (int j = 0; j < BATCH; ++j) {
       const int f = rg + NG * (r0 + j);
       if (r0 + j < RPT && f < F) {
-        const f32x4 s = rows[j] + sfk[f] * vv;
+        const f32x4 s = rows[j] * g + sfk[f] * vv;
         *reinterpret_cast<f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq) = s;
         acc += sfq[f] * s;
       }
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   for (int j = 0; j < ZPT; ++j) {
     const int f = tid + 256 * j;
     if (f < F) {
-      const float zz = zv[j] + sfk[f];
+      const float zz = zv[j] * g + sfk[f];
       zh[f] = zz;
       dpart += sfq[f] * zz;
     }

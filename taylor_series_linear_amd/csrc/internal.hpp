@@ -38,11 +38,14 @@ struct PrefillArgs {
   int L;        // tokens per segment (multiple of C)
   float inv_a;
   int defer_state;  // final state goes through `fin`, then a copy kernel
+  int decay;        // constant decay gamma < 1 (generic kernel only)
+  float log2g;      // log2(gamma)
 };
 
 // Plans a prefill of BH heads x N tokens. Returns false when
-// (d, dv, n_terms, bf16) is not instantiated.
-bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillPlan* plan);
+// (d, dv, n_terms, bf16) is not instantiated. `decay` selects the kernel
+// family that supports a decayed state (the generic one).
+bool prefill_plan(int d, int dv, int n_terms, bool bf16, bool decay, int BH, int N, PrefillPlan* plan);
 
 // Enqueue the whole prefill for one instantiation. Returns hipSuccess or the
 // launch error.
@@ -74,6 +77,7 @@ struct DecodeArgs {
   int out_bf16;
   int BH;
   float inv_a;
+  float gamma;  // decay of the state before the write (1: none)
 };
 
 hipError_t decode_launch(int d, int dv, int n_terms, bool bf16, const DecodeArgs& a,

@@ -469,7 +469,8 @@ __device__ __forceinline__ void gen_table(int w, int lane, int f0, const typenam
 // inside the last 32-key step are written as zeros.
 template <class Cfg, int R>
 __device__ __forceinline__ void score_tiles(const typename Cfg::E* sK, const typename Cfg::E* sQ,
-                                            typename Cfg::E* sP, int c, int g4, float inv_a) {
+                                            typename Cfg::E* sP, int c, int g4, float inv_a, bool decay,
+                                            float log2g) {
   using M = typename Cfg::M;
   using frag = typename M::frag;
   using half = typename M::half;
@@ -519,7 +520,9 @@ __device__ __forceinline__ void score_tiles(const typename Cfg::E* sK, const typ
       float wv = 0.f;
       if constexpr (kt <= qt) {
         wv = taylor_poly<Cfg::NT>(acc[j][i] * inv_a);
-        if (kt == qt && 4 * g4 + i > c) wv = 0.f;  // causal mask (key > query)
+        const int lag = 16 * (qt - kt) + c - 4 * g4 - i;  // query - key
+        if (kt == qt && lag < 0) wv = 0.f;                // causal mask (key > query)
+        if (decay && lag > 0) wv *= exp2f(static_cast<float>(lag) * log2g);
       }
       dst[i] = M::cvt(wv);
     }
@@ -532,7 +535,7 @@ __device__ __forceinline__ void score_tiles(const typename Cfg::E* sK, const typ
 
 enum { MODE_SEGSUM = 0, MODE_MAIN = 1 };
 
-template <class Cfg, int MODE>
+template <class Cfg, int MODE, bool DEC>
 __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   using M = typename Cfg::M;
   using E = typename Cfg::E;
@@ -604,6 +607,12 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           }
           S[ft][i] = val;
         }
+      if (DEC && p > 0) {
+        // S0 is the state just before token 0; this segment starts at t0
+        const float g0 = exp2f(static_cast<float>(p) * static_cast<float>(a.L) * a.log2g);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) S[ft] *= g0;
+      }
     }
     // sum of the earlier segments' states, PB segments' loads in flight at once
     const int PS = a.P - 1;
@@ -622,8 +631,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < PB; ++j)
         if (pp + j < p) {
+          // segment q = pp + j ends L (p - 1 - q) tokens before this one starts
+          const float gq = DEC ? exp2f(static_cast<float>(p - 1 - pp - j) * static_cast<float>(a.L) * a.log2g)
+                                   : 1.f;
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft) S[ft] += t[j][ft];
+          for (int ft = 0; ft < FT; ++ft) S[ft] += gq * t[j][ft];
         }
     }
   }
@@ -752,7 +764,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     }
     if (want_out && gsl == 0) {
       static_for<0, NW>([&](auto ri) {
-        if (w == decltype(ri)::value) score_tiles<Cfg, decltype(ri)::value>(sK, sQ, sP, c, g4, inv_a);
+        if (w == decltype(ri)::value)
+          score_tiles<Cfg, decltype(ri)::value>(sK, sQ, sP, c, g4, inv_a, DEC, a.log2g);
       });
     }
     __syncthreads();
@@ -787,6 +800,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[qt] = M::step(sa, bq[t & 1][qt], acc[qt]);
+      }
+      if constexpr (DEC) {
+        // the state read out by query i of the chunk is i + 1 steps old
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt] *= exp2f(static_cast<float>(16 * qt + c + 1) * a.log2g);
       }
       // intra-chunk term: O^T += [V,1]^T P^T (first slice only); all P^T
       // fragments are fetched before the MFMAs.
@@ -857,13 +875,30 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     if (do_update) {
       // S[:, dv tile w] += phi(K)^T [V,1][:, dv tile w]; the phi(K)^T
       // fragments of feature tile ft+1 are fetched before the MFMAs of ft.
+      // With a decay: S = g^nv S + sum_j g^(nv-1-j) phi(k_j) [v_j, 1].
+      frag bu[KSC];
+#pragma unroll
+      for (int u = 0; u < KSC; ++u) bu[u] = bv[u];
+      if constexpr (DEC) {
+        const float gs = exp2f(static_cast<float>(nv) * a.log2g);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) S[ft] *= gs;
+#pragma unroll
+        for (int u = 0; u < KSC; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int key = 32 * u + 8 * g4 + j;
+            const float f = key < nv ? exp2f(static_cast<float>(nv - 1 - key) * a.log2g) : 0.f;
+            bu[u][j] = M::cvt(static_cast<float>(bv[u][j]) * f);
+          }
+      }
       if constexpr (Cfg::KH) {
         // fp16 contraction: u(KS K)^T from the key table, [V,1] converted
         f16x8 bvh[KSC], ak[2][KSC];
 #pragma unroll
         for (int u = 0; u < KSC; ++u)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) bvh[u][j] = static_cast<_Float16>(static_cast<float>(bv[u][j]));
+          for (int j = 0; j < 8; ++j) bvh[u][j] = static_cast<_Float16>(static_cast<float>(bu[u][j]));
 #pragma unroll
         for (int u = 0; u < KSC; ++u) ak[0][u] = *reinterpret_cast<const f16x8*>(sPK + c * Cfg::PK + 32 * u + 8 * g4);
 #pragma unroll
@@ -890,7 +925,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
               ak[(ft + 1) & 1][u] = lds_frag8(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
           }
 #pragma unroll
-          for (int u = 0; u < KSC; ++u) S[ft] = M::step(ak[ft & 1][u], bv[u], S[ft]);
+          for (int u = 0; u < KSC; ++u) S[ft] = M::step(ak[ft & 1][u], bu[u], S[ft]);
         }
       }
     }
@@ -999,13 +1034,21 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   auto blocks_for = [](int units) { return 8 * G * ((units + 7) / 8); };
   if (a.P > 1) {
     const int units = a.BH * (a.P - 1);
-    hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_SEGSUM>), dim3(blocks_for(units)), dim3(Cfg::NTHR), 0,
-                       stream, a);
+    if (a.decay)
+      hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_SEGSUM, true>), dim3(blocks_for(units)), dim3(Cfg::NTHR), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_SEGSUM, false>), dim3(blocks_for(units)), dim3(Cfg::NTHR), 0,
+                         stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_MAIN>), dim3(blocks_for(a.BH * a.P)), dim3(Cfg::NTHR), 0,
-                     stream, a);
+  if (a.decay)
+    hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_MAIN, true>), dim3(blocks_for(a.BH * a.P)), dim3(Cfg::NTHR), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_MAIN, false>), dim3(blocks_for(a.BH * a.P)), dim3(Cfg::NTHR), 0,
+                       stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.defer_state) {
@@ -1032,6 +1075,7 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(16, 64, 1, false, 32, 64, true)         \
   X(16, 16, 3, true, 160, 64, true)         \
   X(16, 16, 3, false, 160, 64, true)        \
+  X(16, 64, 3, true, 160, 64, true)         \
   X(16, 64, 3, false, 160, 64, true)        \
   X(16, 16, 5, true, 608, 32, false)        \
   X(16, 16, 5, false, 256, 32, false)       \
@@ -1051,7 +1095,8 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(64, 64, 1, false, 32, 64, true)         \
   X(64, 16, 3, true, 544, 32, false)        \
   X(64, 16, 3, false, 128, 32, false)       \
-  X(64, 64, 3, false, 128, 32, false)
+  X(64, 64, 3, false, 128, 32, false)       \
+  X(64, 64, 3, true, 256, 32, false)
 
 // Sequence split for the generic kernels: enough workgroups (heads x
 // segments x slices) to give each compute unit about two, and at least 4
@@ -1091,9 +1136,9 @@ static bool is_o2(int d, int dv, int n_terms, bool bf16) {
   return d == 16 && dv == 64 && n_terms == 3 && bf16;
 }
 
-bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillPlan* plan) {
-  if (is_o2(d, dv, n_terms, bf16)) return o2::plan(BH, N, plan);
-  if (is_w2(d, dv, n_terms, bf16)) return w2::plan(BH, N, plan);
+bool prefill_plan(int d, int dv, int n_terms, bool bf16, bool decay, int BH, int N, PrefillPlan* plan) {
+  if (!decay && is_o2(d, dv, n_terms, bf16)) return o2::plan(BH, N, plan);
+  if (!decay && is_w2(d, dv, n_terms, bf16)) return w2::plan(BH, N, plan);
 #define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
   if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_) {             \
     plan_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(BH, N, plan);          \
@@ -1106,8 +1151,8 @@ bool prefill_plan(int d, int dv, int n_terms, bool bf16, int BH, int N, PrefillP
 
 hipError_t prefill_launch(int d, int dv, int n_terms, bool bf16, const PrefillArgs& a,
                           hipStream_t stream) {
-  if (is_o2(d, dv, n_terms, bf16)) return o2::launch(a, stream);
-  if (is_w2(d, dv, n_terms, bf16)) return w2::launch(a, stream);
+  if (!a.decay && is_o2(d, dv, n_terms, bf16)) return o2::launch(a, stream);
+  if (!a.decay && is_w2(d, dv, n_terms, bf16)) return w2::launch(a, stream);
 #define X(D_, DV_, NT_, BF_, FS_, C_, UN_)                                 \
   if (d == D_ && dv == DV_ && n_terms == NT_ && bf16 == BF_)               \
     return launch_cfg<PCfg<D_, DV_, NT_, BF_, FS_, C_, UN_>>(a, stream);

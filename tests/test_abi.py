@@ -18,7 +18,9 @@ def test_every_declared_function_is_exported():
     names = tl.header_functions()
     assert set(names) == {"taylor_feature_dim", "taylor_is_supported", "taylor_last_error",
                           "taylor_feature_map", "taylor_attn_prefill_workspace",
-                          "taylor_attn_prefill", "taylor_attn_decode"}
+                          "taylor_attn_prefill", "taylor_attn_decode",
+                          "taylor_attn_prefill_decayed_workspace", "taylor_attn_prefill_decayed",
+                          "taylor_attn_decode_decayed"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -131,3 +133,30 @@ def test_python_wrapper_maps_statuses():
         tl.check(TAYLOR_ERR_BAD_SHAPE)
     with pytest.raises(RuntimeError):
         tl.check(TAYLOR_ERR_WORKSPACE)
+
+
+def test_decayed_entry_points_reject_bad_arguments():
+    def pre(gamma, **kw):
+        args = dict(in_dtype=TAYLOR_BF16, n=3, d=16, ws=None, ws_bytes=0, B=1, H=2, N=64)
+        args.update(kw)
+        return L.taylor_attn_prefill_decayed(FAKE, FAKE, FAKE, args["in_dtype"], args["B"], args["H"], args["N"],
+                                             args["d"], 64,
+                                             args["n"], 4.0, gamma, None, None, FAKE, TAYLOR_BF16, None, None,
+                                             args["ws"], args["ws_bytes"], None)
+
+    def dec(gamma, **kw):
+        return L.taylor_attn_decode_decayed(FAKE, FAKE, FAKE, TAYLOR_F32, 2, 3, 16, 64, kw.get("n", 3), 4.0, gamma,
+                                            FAKE, FAKE, FAKE, TAYLOR_F32, None)
+
+    for g in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert pre(g) == TAYLOR_ERR_BAD_SCALE
+        assert b"gamma" in L.taylor_last_error()
+        assert dec(g) == TAYLOR_ERR_BAD_SCALE
+    assert pre(0.9, n=4) == TAYLOR_ERR_UNSUPPORTED
+    assert dec(0.9, n=2) == TAYLOR_ERR_UNSUPPORTED
+    # the decayed prefill runs the generic kernels: its own workspace size
+    need = L.taylor_attn_prefill_decayed_workspace(2, 8, 8192, 16, 64, 3, TAYLOR_BF16)
+    assert need != ctypes.c_size_t(-1).value
+    assert need > 0
+    assert pre(0.9, B=2, H=8, N=8192, ws=FAKE, ws_bytes=need - 1) == TAYLOR_ERR_WORKSPACE
+    assert L.taylor_attn_prefill_decayed_workspace(1, 1, 64, 16, 64, 2, TAYLOR_BF16) == ctypes.c_size_t(-1).value
