@@ -93,6 +93,56 @@ def _alpha_no_factorial(d, n_terms, a):
     return np.array(out)
 
 
+def _direct_decay_bug(kind):
+    """Decayed direct form with one planted mistake: 'den' leaves the
+    denominator undecayed, 's0' carries S0 with gamma^t instead of gamma^(t+1)."""
+    def f(q, k, v, n_terms, a, S0=None, z0=None, rows=None, block=256, gamma=1.0):
+        q = np.asarray(q, dtype=np.float64)
+        if q.ndim > 2 or gamma == 1.0:
+            return _orig_direct(q, k, v, n_terms, a, S0, z0, rows, block, gamma)
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        N = q.shape[0]
+        r = np.arange(N) if rows is None else np.asarray(rows)
+        W = T.taylor_weight(q[r] @ k.T / a, n_terms)
+        lag = r[:, None] - np.arange(N)[None, :]
+        W = np.where(lag >= 0, W, 0.0)
+        Wd = W * np.power(gamma, np.maximum(lag, 0).astype(np.float64))
+        num = Wd @ v
+        den = (W if kind == "den" else Wd).sum(1)
+        if S0 is not None:
+            fq = T.phi(q[r], n_terms) * T.alpha_vector(q.shape[1], n_terms, a)
+            carry = np.power(gamma, r + (0.0 if kind == "s0" else 1.0))
+            num = num + carry[:, None] * (fq @ np.asarray(S0))
+            den = den + carry * (fq @ np.asarray(z0))
+        return num / den[:, None]
+    return f
+
+
+_orig_recurrent = T.recurrent
+
+
+def _recurrent_decay_after_write(q, k, v, n_terms, a, S0=None, z0=None, gamma=1.0):
+    if gamma == 1.0:
+        return _orig_recurrent(q, k, v, n_terms, a, S0, z0)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, d = q.shape
+    F = T.n_features(d, n_terms)
+    S = np.zeros((F, v.shape[1])) if S0 is None else np.array(S0, dtype=np.float64)
+    z = np.zeros(F) if z0 is None else np.array(z0, dtype=np.float64)
+    alpha = T.alpha_vector(d, n_terms, a)
+    out = np.empty((N, v.shape[1]))
+    for t in range(N):
+        fk = T.phi(k[t:t + 1], n_terms)[0]
+        S = gamma * (S + np.outer(fk, v[t]))
+        z = gamma * (z + fk)
+        fq = T.phi(q[t:t + 1], n_terms)[0] * alpha
+        out[t] = (fq @ S) / (fq @ z)
+    return out, S, z
+
+
 def _alignment_printed(N, w, distractor_t=-1.0):
     return -1 + math.sqrt(2 * (N - 1) * w / (1 - w) - 1)
 
@@ -107,6 +157,9 @@ MUTATIONS = {
     "recurrent_reads_before_update": ("recurrent", _recurrent_read_first),
     "alpha_without_factorials": ("alpha_vector", _alpha_no_factorial),
     "alignment_printed_formula": ("required_alignment_based", _alignment_printed),
+    "decay_leaves_denominator": ("direct", _direct_decay_bug("den")),
+    "decay_initial_state_one_step_short": ("direct", _direct_decay_bug("s0")),
+    "decay_after_the_write": ("recurrent", _recurrent_decay_after_write),
 }
 
 
