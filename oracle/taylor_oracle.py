@@ -33,6 +33,11 @@ Readings taken where the pages leave a step open:
   applied at read-out (or folded into phi(q) when ``a`` is passed to phi).
 * Canonical feature order: m ascending; within an order, non-decreasing
   index tuples in lexicographic order.
+* Query/key preprocessing (``preprocess``): EA treats unit-sphere rows as
+  mandatory and cites per-head temperatures; the reading taken divides each
+  row by its l2 norm (a zero row stays zero), then multiplies queries by a
+  scale and a per-head factor and keys by a scale. The method then runs on
+  the preprocessed rows.
 * Decay (``gamma``): one constant factor gamma in (0, 1] for every step,
   applied to S and z alike (z is the state of the all-ones value column), so
   the output stays a normalised average: token s enters the output at time
@@ -293,6 +298,24 @@ def exact_fraction(q, k, v, n_terms: int, a) -> list[list[Fraction]]:
             num = [nu + w * vj for nu, vj in zip(num, v[s])]
         out.append([nu / den for nu in num])
     return out
+
+
+# --------------------------------------------------------------------------
+# Query/key preprocessing (EA: rows on the unit sphere; per-head temperature)
+# --------------------------------------------------------------------------
+
+def preprocess(x, normalise: bool = True, scale: float = 1.0, head_scale=None) -> np.ndarray:
+    """Rows of x [..., H, N, d] (or [N, d]) divided by their l2 norm (zero rows
+    stay zero), times ``scale`` and, per head, ``head_scale[h]`` (x[..., h, :, :])."""
+    x = np.asarray(x, dtype=np.float64)
+    if normalise:
+        n = np.linalg.norm(x, axis=-1, keepdims=True)
+        x = np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    x = x * float(scale)
+    if head_scale is not None:
+        hs = np.asarray(head_scale, dtype=np.float64)
+        x = x * hs.reshape(hs.shape + (1, 1))
+    return x
 
 
 # --------------------------------------------------------------------------

@@ -479,3 +479,25 @@ def test_decay_continuation_through_state():
     assert rel(part, whole) < 1e-13
     o, S, z = T.decode_step(q[N1], k[N1], v[N1], S0, z0, 3, a, gamma=g)
     assert rel(o, whole[0]) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# Query/key preprocessing (EA: unit-sphere rows are mandatory; temperatures)
+# ----------------------------------------------------------------------------
+
+def test_preprocess_pins():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((3, 10, 16))  # [H, N, d]
+    x[1, 4] = 0.0                          # a zero row stays zero
+    hs = np.array([0.5, 2.0, 3.0])
+    y = T.preprocess(x, True, 2.0, hs)
+    norms = np.linalg.norm(y, axis=-1)
+    want = 2.0 * hs[:, None] * np.ones((3, 10))
+    want[1, 4] = 0.0
+    assert np.max(np.abs(norms - want)) < 1e-14
+    # direction kept, positive rescaling of the input removed
+    cos = np.sum(y * x, axis=-1) / np.maximum(norms * np.linalg.norm(x, axis=-1), 1e-300)
+    assert np.max(np.abs(cos[norms > 0] - 1)) < 1e-14
+    assert rel(T.preprocess(7.5 * x, True, 2.0, hs), y) < 1e-15
+    # without normalisation it is a plain rescaling
+    assert rel(T.preprocess(x, False, 3.0), 3.0 * x) == 0
