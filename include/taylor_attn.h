@@ -182,6 +182,46 @@ taylor_status taylor_attn_decode_decayed(const void* q, const void* k, const voi
                                          int n_terms, float a, float gamma, float* S, float* z, void* o,
                                          taylor_dtype out_dtype, void* stream);
 
+/*
+ * Extended options: the decay above plus query/key preprocessing fused into
+ * the kernels. "Expanding Attention" (defaults paragraph, "Two
+ * prerequisites") runs on queries and keys normalised to the unit sphere and
+ * calls this mandatory; the related work it cites adds a per-head
+ * temperature. With qk_norm set, every q and k row is divided by its l2 norm
+ * (a zero row stays zero); then q is multiplied by q_scale and, per head h,
+ * by q_head_scale[h], and k by k_scale. The method runs on those rows. For
+ * bf16 inputs the preprocessed rows are rounded to bf16 inside the kernels.
+ *   gamma         0 < gamma <= 1 (1: no decay)
+ *   qk_norm       0 or 1
+ *   q_scale       finite, > 0 (1: none)
+ *   k_scale       finite, > 0 (1: none)
+ *   q_head_scale  device pointer to H floats, or NULL (all 1); read by the
+ *                 kernels, not checked
+ * Invalid gamma or scales return TAYLOR_ERR_BAD_SCALE; a NULL ext returns
+ * TAYLOR_ERR_NULL_PTR. Everything else is as for taylor_attn_prefill and
+ * taylor_attn_decode; the prefill workspace is sized by
+ * taylor_attn_prefill_ext_workspace (the same size as for the decayed call).
+ */
+typedef struct taylor_attn_ext {
+  float gamma;
+  int qk_norm;
+  float q_scale;
+  float k_scale;
+  const float* q_head_scale;
+} taylor_attn_ext;
+
+size_t taylor_attn_prefill_ext_workspace(int B, int H, int N, int d, int dv, int n_terms,
+                                         taylor_dtype in_dtype);
+taylor_status taylor_attn_prefill_ext(const void* q, const void* k, const void* v,
+                                      taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                      int n_terms, float a, const taylor_attn_ext* ext,
+                                      const float* S0, const float* z0, void* o, taylor_dtype out_dtype,
+                                      float* S, float* z, void* workspace, size_t ws_bytes, void* stream);
+taylor_status taylor_attn_decode_ext(const void* q, const void* k, const void* v,
+                                     taylor_dtype in_dtype, int B, int H, int d, int dv, int n_terms,
+                                     float a, const taylor_attn_ext* ext, float* S, float* z, void* o,
+                                     taylor_dtype out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

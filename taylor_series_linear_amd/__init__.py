@@ -28,6 +28,12 @@ TAYLOR_BF16 = 1
 _lib = None
 
 
+class Ext(ctypes.Structure):
+    """taylor_attn_ext: decay and query/key preprocessing options."""
+    _fields_ = [("gamma", ctypes.c_float), ("qk_norm", ctypes.c_int), ("q_scale", ctypes.c_float),
+                ("k_scale", ctypes.c_float), ("q_head_scale", ctypes.c_void_p)]
+
+
 class TaylorError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"taylor_attn status {status}: {msg}")
@@ -75,6 +81,15 @@ def lib() -> ctypes.CDLL:
     L.taylor_attn_decode_decayed.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32,
                                              vp, vp, vp, i32, vp]
     L.taylor_attn_decode_decayed.restype = i32
+    ep = ctypes.POINTER(Ext)
+    L.taylor_attn_prefill_ext_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.taylor_attn_prefill_ext_workspace.restype = sz
+    L.taylor_attn_prefill_ext.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, ep,
+                                          vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.taylor_attn_prefill_ext.restype = i32
+    L.taylor_attn_decode_ext.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, ep,
+                                         vp, vp, vp, i32, vp]
+    L.taylor_attn_decode_ext.restype = i32
     del fp
     _lib = L
     return L
@@ -164,16 +179,32 @@ def prefill_workspace_bytes(B, H, N, d, dv, n_terms, in_dtype, decayed: bool = F
     return int(r)
 
 
+def _ext(gamma, qk_norm, q_scale, k_scale, q_head_scale, H):
+    """The options struct, or None when every option is at its default."""
+    if gamma is None and not qk_norm and q_scale == 1.0 and k_scale == 1.0 and q_head_scale is None:
+        return None
+    hp = None
+    if q_head_scale is not None:
+        _need(q_head_scale, "q_head_scale")
+        if q_head_scale.dtype != _torch().float32 or q_head_scale.dim() != 1 or q_head_scale.numel() != H:
+            raise ValueError(f"q_head_scale must be a float32 tensor [H] = [{H}]")
+        hp = q_head_scale.data_ptr()
+    return Ext(1.0 if gamma is None else float(gamma), 1 if qk_norm else 0, float(q_scale), float(k_scale), hp)
+
+
 def prefill(q, k, v, n_terms: int, a: float, S0=None, z0=None, *, out_dtype=None,
             want_output: bool = True, return_state: bool = False, S=None, z=None,
-            workspace=None, gamma: float | None = None):
+            workspace=None, gamma: float | None = None, qk_norm: bool = False, q_scale: float = 1.0,
+            k_scale: float = 1.0, q_head_scale=None):
     """Causal prefill. q, k [B, H, N, d], v [B, H, N, dv] (float32 or bfloat16, same dtype).
 
     Returns o [B, H, N, dv] (out_dtype, default q.dtype) or None, and with
     return_state=True also the final state (S [B, H, F, dv], z [B, H, F], float32).
     S / z may be passed to write the state into given buffers (they may be S0 / z0).
     With ``gamma`` (0 < gamma <= 1) the state decays by gamma before every
-    write (taylor_attn_prefill_decayed).
+    write; ``qk_norm``, ``q_scale``, ``k_scale`` and ``q_head_scale`` (a float32
+    tensor [H]) preprocess q and k rows inside the kernels
+    (taylor_attn_prefill_ext).
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -195,28 +226,31 @@ def prefill(q, k, v, n_terms: int, a: float, S0=None, z0=None, *, out_dtype=None
             _need(t, n)
             if t.dtype != torch.float32:
                 raise ValueError(f"{n} must be float32")
-    ws_bytes = prefill_workspace_bytes(B, H, N, d, dv, n_terms, q.dtype, decayed=gamma is not None)
+    ext = _ext(gamma, qk_norm, q_scale, k_scale, q_head_scale, H)
+    ws_bytes = prefill_workspace_bytes(B, H, N, d, dv, n_terms, q.dtype, decayed=ext is not None)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
     od = TAYLOR_F32 if o is None else _dt(o)
-    if gamma is None:
+    if ext is None:
         check(lib().taylor_attn_prefill(
             _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, dv, n_terms, float(a),
             _ptr(S0), _ptr(z0), _ptr(o), od, _ptr(S), _ptr(z), _ptr(workspace), ws_len, _stream()))
     else:
-        check(lib().taylor_attn_prefill_decayed(
-            _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, dv, n_terms, float(a), float(gamma),
+        check(lib().taylor_attn_prefill_ext(
+            _ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, N, d, dv, n_terms, float(a), ctypes.byref(ext),
             _ptr(S0), _ptr(z0), _ptr(o), od, _ptr(S), _ptr(z), _ptr(workspace), ws_len, _stream()))
     if return_state or S is not None:
         return o, S, z
     return o
 
 
-def decode(q, k, v, S, z, n_terms: int, a: float, *, out_dtype=None, o=None, gamma: float | None = None):
+def decode(q, k, v, S, z, n_terms: int, a: float, *, out_dtype=None, o=None, gamma: float | None = None,
+           qk_norm: bool = False, q_scale: float = 1.0, k_scale: float = 1.0, q_head_scale=None):
     """One decode step: q, k [B, H, d], v [B, H, dv]; S, z updated in place. Returns o [B, H, dv].
 
-    With ``gamma`` the state decays by gamma before the write (taylor_attn_decode_decayed)."""
+    With ``gamma`` the state decays by gamma before the write; the other
+    options preprocess q and k as for prefill (taylor_attn_decode_ext)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (S, "S"), (z, "z")):
         _need(t, n)
@@ -224,11 +258,12 @@ def decode(q, k, v, S, z, n_terms: int, a: float, *, out_dtype=None, o=None, gam
     dv = v.shape[-1]
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
-    if gamma is None:
+    ext = _ext(gamma, qk_norm, q_scale, k_scale, q_head_scale, H)
+    if ext is None:
         check(lib().taylor_attn_decode(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, d, dv, n_terms,
                                        float(a), _ptr(S), _ptr(z), _ptr(o), _dt(o), _stream()))
     else:
-        check(lib().taylor_attn_decode_decayed(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, d, dv, n_terms,
-                                               float(a), float(gamma), _ptr(S), _ptr(z), _ptr(o), _dt(o),
-                                               _stream()))
+        check(lib().taylor_attn_decode_ext(_ptr(q), _ptr(k), _ptr(v), _dt(q), B, H, d, dv, n_terms,
+                                           float(a), ctypes.byref(ext), _ptr(S), _ptr(z), _ptr(o), _dt(o),
+                                           _stream()))
     return o

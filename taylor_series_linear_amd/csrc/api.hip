@@ -53,6 +53,25 @@ taylor_status check_gamma(float g) {
   return TAYLOR_OK;
 }
 
+taylor_status check_ext(const taylor_attn_ext* x) {
+  taylor_status s = check_gamma(x->gamma);
+  if (s != TAYLOR_OK) return s;
+  if (!std::isfinite(x->q_scale) || !(x->q_scale > 0.f) || !std::isfinite(x->k_scale) || !(x->k_scale > 0.f))
+    return fail(TAYLOR_ERR_BAD_SCALE, "q_scale and k_scale must be finite and > 0");
+  return TAYLOR_OK;
+}
+
+// Options of the plain entry points' decayed variants.
+taylor_attn_ext decay_only(float gamma) {
+  taylor_attn_ext x{};
+  x.gamma = gamma;
+  x.qk_norm = 0;
+  x.q_scale = 1.f;
+  x.k_scale = 1.f;
+  x.q_head_scale = nullptr;
+  return x;
+}
+
 taylor_status check_dtype(taylor_dtype t, const char* what) {
   if (t != TAYLOR_F32 && t != TAYLOR_BF16)
     return fail(TAYLOR_ERR_UNSUPPORTED, std::string(what) + " must be TAYLOR_F32 or TAYLOR_BF16");
@@ -146,15 +165,16 @@ namespace {
 // family (the decayed one also runs gamma = 1, so its workspace size does not
 // depend on gamma).
 taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B, int H,
-                           int N, int d, int dv, int n_terms, float a, bool decay, float gamma, const float* S0,
+                           int N, int d, int dv, int n_terms, float a, const taylor_attn_ext* ext, const float* S0,
                            const float* z0, void* o, taylor_dtype out_dtype, float* S, float* z,
                            void* workspace, size_t ws_bytes, void* stream) {
   tl::PrefillPlan p;
-  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, decay, &p);
+  const bool extk = ext != nullptr;
+  taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, extk, &p);
   if (s != TAYLOR_OK) return s;
   if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
   if ((s = check_scale(a)) != TAYLOR_OK) return s;
-  if (decay && (s = check_gamma(gamma)) != TAYLOR_OK) return s;
+  if (extk && (s = check_ext(ext)) != TAYLOR_OK) return s;
   if ((S0 == nullptr) != (z0 == nullptr))
     return fail(TAYLOR_ERR_NULL_PTR, "S0 and z0 must both be given or both be NULL");
   if ((S == nullptr) != (z == nullptr))
@@ -197,22 +217,27 @@ taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_d
   // while the last one finishes the state, so the final state goes through
   // the workspace and is copied out afterwards.
   args.defer_state = (S != nullptr && p.P > 1 && (S == S0 || z == z0)) ? 1 : 0;
-  args.decay = decay ? 1 : 0;
-  args.log2g = decay ? std::log2(gamma) : 0.f;
+  args.decay = extk ? 1 : 0;
+  args.log2g = extk ? std::log2(ext->gamma) : 0.f;
+  args.qk_norm = extk ? (ext->qk_norm != 0) : 0;
+  args.q_scale = extk ? ext->q_scale : 1.f;
+  args.k_scale = extk ? ext->k_scale : 1.f;
+  args.q_head_scale = extk ? ext->q_head_scale : nullptr;
+  args.H = H;
   return hip_status(tl::prefill_launch(d, dv, n_terms, in_dtype == TAYLOR_BF16, args, st),
                     "taylor_attn_prefill launch");
 }
 
 taylor_status decode_impl(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B, int H,
-                          int d, int dv, int n_terms, float a, float gamma, float* S, float* z, void* o,
-                          taylor_dtype out_dtype, void* stream) {
+                          int d, int dv, int n_terms, float a, const taylor_attn_ext& ext, float* S, float* z,
+                          void* o, taylor_dtype out_dtype, void* stream) {
   taylor_status s = check_dtype(in_dtype, "in_dtype");
   if (s != TAYLOR_OK) return s;
   if ((s = check_dtype(out_dtype, "out_dtype")) != TAYLOR_OK) return s;
   if (B < 0 || H < 0) return fail(TAYLOR_ERR_BAD_SHAPE, "B and H must be >= 0");
   if ((s = check_dn(d, dv, n_terms, true)) != TAYLOR_OK) return s;
   if ((s = check_scale(a)) != TAYLOR_OK) return s;
-  if ((s = check_gamma(gamma)) != TAYLOR_OK) return s;
+  if ((s = check_ext(&ext)) != TAYLOR_OK) return s;
   if (checked_mul({B, H}) > INT32_MAX)
     return fail(TAYLOR_ERR_BAD_SHAPE, "B*H exceeds the grid limit");
   const int BH = B * H;
@@ -229,7 +254,12 @@ taylor_status decode_impl(const void* q, const void* k, const void* v, taylor_dt
   args.out_bf16 = out_dtype == TAYLOR_BF16;
   args.BH = BH;
   args.inv_a = 1.0f / a;
-  args.gamma = gamma;
+  args.gamma = ext.gamma;
+  args.qk_norm = ext.qk_norm != 0;
+  args.q_scale = ext.q_scale;
+  args.k_scale = ext.k_scale;
+  args.q_head_scale = ext.q_head_scale;
+  args.H = H;
   (void)hipGetLastError();
   return hip_status(tl::decode_launch(d, dv, n_terms, in_dtype == TAYLOR_BF16, args,
                                       static_cast<hipStream_t>(stream)),
@@ -253,7 +283,7 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   int n_terms, float a, const float* S0, const float* z0,
                                   void* o, taylor_dtype out_dtype, float* S, float* z,
                                   void* workspace, size_t ws_bytes, void* stream) {
-  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, false, 1.f, S0, z0, o, out_dtype, S, z,
+  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, nullptr, S0, z0, o, out_dtype, S, z,
                       workspace, ws_bytes, stream);
 }
 
@@ -270,22 +300,43 @@ taylor_status taylor_attn_prefill_decayed(const void* q, const void* k, const vo
                                           int n_terms, float a, float gamma, const float* S0,
                                           const float* z0, void* o, taylor_dtype out_dtype, float* S,
                                           float* z, void* workspace, size_t ws_bytes, void* stream) {
-  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, true, gamma, S0, z0, o, out_dtype, S, z,
-                      workspace, ws_bytes, stream);
+  const taylor_attn_ext x = decay_only(gamma);
+  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, &x, S0, z0, o, out_dtype, S, z, workspace,
+                      ws_bytes, stream);
+}
+
+size_t taylor_attn_prefill_ext_workspace(int B, int H, int N, int d, int dv, int n_terms, taylor_dtype in_dtype) {
+  return taylor_attn_prefill_decayed_workspace(B, H, N, d, dv, n_terms, in_dtype);
+}
+
+taylor_status taylor_attn_prefill_ext(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B,
+                                      int H, int N, int d, int dv, int n_terms, float a, const taylor_attn_ext* ext,
+                                      const float* S0, const float* z0, void* o, taylor_dtype out_dtype, float* S,
+                                      float* z, void* workspace, size_t ws_bytes, void* stream) {
+  if (ext == nullptr) return fail(TAYLOR_ERR_NULL_PTR, "ext is required");
+  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, ext, S0, z0, o, out_dtype, S, z, workspace,
+                      ws_bytes, stream);
 }
 
 taylor_status taylor_attn_decode(const void* q, const void* k, const void* v,
                                  taylor_dtype in_dtype, int B, int H, int d, int dv,
                                  int n_terms, float a, float* S, float* z, void* o,
                                  taylor_dtype out_dtype, void* stream) {
-  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, 1.f, S, z, o, out_dtype, stream);
+  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, decay_only(1.f), S, z, o, out_dtype, stream);
 }
 
 taylor_status taylor_attn_decode_decayed(const void* q, const void* k, const void* v,
                                          taylor_dtype in_dtype, int B, int H, int d, int dv,
                                          int n_terms, float a, float gamma, float* S, float* z, void* o,
                                          taylor_dtype out_dtype, void* stream) {
-  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, gamma, S, z, o, out_dtype, stream);
+  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, decay_only(gamma), S, z, o, out_dtype, stream);
+}
+
+taylor_status taylor_attn_decode_ext(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B,
+                                     int H, int d, int dv, int n_terms, float a, const taylor_attn_ext* ext, float* S,
+                                     float* z, void* o, taylor_dtype out_dtype, void* stream) {
+  if (ext == nullptr) return fail(TAYLOR_ERR_NULL_PTR, "ext is required");
+  return decode_impl(q, k, v, in_dtype, B, H, d, dv, n_terms, a, *ext, S, z, o, out_dtype, stream);
 }
 
 }  // extern "C"

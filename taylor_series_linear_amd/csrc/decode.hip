@@ -83,6 +83,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   if (tid < DV) sv[tid] = load_in<BF16>(a.v, static_cast<size_t>(bh) * DV + tid);
   __syncthreads();
 
+  // query/key preprocessing: row l2-normalisation and scales (factors on
+  // every coordinate)
+  float fq = a.q_scale * (a.q_head_scale != nullptr ? a.q_head_scale[bh % a.H] : 1.f);
+  float fk = a.k_scale;
+  if (a.qk_norm) {
+    float nq = 0.f, nk = 0.f;
+    for (int j = 0; j < D; ++j) {
+      nq += sq[j] * sq[j];
+      nk += sk[j] * sk[j];
+    }
+    fq = nq > 0.f ? fq / __builtin_sqrtf(nq) : 0.f;
+    fk = nk > 0.f ? fk / __builtin_sqrtf(nk) : 0.f;
+  }
+  const float cq = fq * inv_a;
+
   const auto& tab = g_dtab<D, NT>;
   for (int f = tid; f < F; f += 256) {
     const PackedFeature e = tab.e[f];
@@ -90,8 +105,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     float pk = e.w, pq = e.w * e.inv_mfact;
     for (int j = 0; j < m; ++j) {
       const int i = (e.idx >> (8 * j)) & 255;
-      pk *= sk[i];
-      pq *= sq[i] * inv_a;
+      pk *= sk[i] * fk;
+      pq *= sq[i] * cq;
     }
     sfk[f] = pk;
     sfq[f] = pq;

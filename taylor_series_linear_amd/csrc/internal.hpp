@@ -38,8 +38,14 @@ struct PrefillArgs {
   int L;        // tokens per segment (multiple of C)
   float inv_a;
   int defer_state;  // final state goes through `fin`, then a copy kernel
-  int decay;        // constant decay gamma < 1 (generic kernel only)
-  float log2g;      // log2(gamma)
+  // extended options (generic kernel family only)
+  int decay;        // extended kernels: decay and query/key preprocessing
+  float log2g;      // log2(gamma) (0: no decay)
+  int qk_norm;      // divide q and k rows by their l2 norm
+  float q_scale;    // then multiply q by q_scale * q_head_scale[h], k by k_scale
+  float k_scale;
+  const float* q_head_scale;  // device [H] or null
+  int H;
 };
 
 // Plans a prefill of BH heads x N tokens. Returns false when
@@ -78,6 +84,11 @@ struct DecodeArgs {
   int BH;
   float inv_a;
   float gamma;  // decay of the state before the write (1: none)
+  int qk_norm;  // query/key preprocessing, as for prefill
+  float q_scale;
+  float k_scale;
+  const float* q_head_scale;
+  int H;
 };
 
 hipError_t decode_launch(int d, int dv, int n_terms, bool bf16, const DecodeArgs& a,

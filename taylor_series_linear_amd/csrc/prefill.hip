@@ -535,7 +535,7 @@ __device__ __forceinline__ void score_tiles(const typename Cfg::E* sK, const typ
 
 enum { MODE_SEGSUM = 0, MODE_MAIN = 1 };
 
-template <class Cfg, int MODE, bool DEC>
+template <class Cfg, int MODE, bool EXT>
 __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   using M = typename Cfg::M;
   using E = typename Cfg::E;
@@ -607,7 +607,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           }
           S[ft][i] = val;
         }
-      if (DEC && p > 0) {
+      if (EXT && p > 0) {
         // S0 is the state just before token 0; this segment starts at t0
         const float g0 = exp2f(static_cast<float>(p) * static_cast<float>(a.L) * a.log2g);
 #pragma unroll
@@ -632,7 +632,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       for (int j = 0; j < PB; ++j)
         if (pp + j < p) {
           // segment q = pp + j ends L (p - 1 - q) tokens before this one starts
-          const float gq = DEC ? exp2f(static_cast<float>(p - 1 - pp - j) * static_cast<float>(a.L) * a.log2g)
+          const float gq = EXT ? exp2f(static_cast<float>(p - 1 - pp - j) * static_cast<float>(a.L) * a.log2g)
                                    : 1.f;
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) S[ft] += gq * t[j][ft];
@@ -694,17 +694,35 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   };
   // Q, K row-major (and, for the table-driven generator, transposed into the
   // coordinate rows of the factor tables); V transposed (key-contiguous) with
-  // the ones row below it.
+  // the ones row below it. Extended kernels first preprocess the Q and K
+  // rows: the D / EV consecutive lanes that hold one row sum its squares
+  // with lane exchanges, then scale their items.
+  const float qhead = (EXT && a.q_head_scale != nullptr) ? a.q_head_scale[bh % a.H] : 1.f;
   auto stage = [&](int nvv) {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int i = tid + s * Cfg::NTHR;
+      uint4 val = pf[s];
+      if constexpr (EXT) {
+        E* e = reinterpret_cast<E*>(&val);
+        float ss = 0.f;
+#pragma unroll
+        for (int u = 0; u < EV; ++u) ss += static_cast<float>(e[u]) * static_cast<float>(e[u]);
+#pragma unroll
+        for (int m = 1; m < D / EV; m <<= 1) ss += __shfl_xor(ss, m);
+        float f = i < QB ? a.q_scale * qhead : a.k_scale;
+        if (a.qk_norm) f = ss > 0.f ? f / __builtin_sqrtf(ss) : 0.f;
+        if (i < QB + NQI && f != 1.f) {
+#pragma unroll
+          for (int u = 0; u < EV; ++u) e[u] = M::cvt(static_cast<float>(e[u]) * f);
+        }
+      }
       if (i < QB) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
         if (want_out) {
-          *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = pf[s];
+          *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = val;
           if constexpr (!Cfg::UNROLL) {
-            const E* e = reinterpret_cast<const E*>(&pf[s]);
+            const E* e = reinterpret_cast<const E*>(&val);
 #pragma unroll
             for (int u = 0; u < EV; ++u) sTQ[(1 + col + u) * Cfg::TP + row] = static_cast<float>(e[u]);
           }
@@ -712,9 +730,9 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       } else if (i < QB + NQI) {
         const int j = i - QB;
         const int row = j / (D / EV), col = (j % (D / EV)) * EV;
-        *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = pf[s];
+        *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = val;
         if constexpr (!Cfg::UNROLL) {
-          const E* e = reinterpret_cast<const E*>(&pf[s]);
+          const E* e = reinterpret_cast<const E*>(&val);
 #pragma unroll
           for (int u = 0; u < EV; ++u) sTK[(1 + col + u) * Cfg::TPK + row] = static_cast<KE>(static_cast<float>(e[u]) * Cfg::KS);
         }
@@ -765,7 +783,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     if (want_out && gsl == 0) {
       static_for<0, NW>([&](auto ri) {
         if (w == decltype(ri)::value)
-          score_tiles<Cfg, decltype(ri)::value>(sK, sQ, sP, c, g4, inv_a, DEC, a.log2g);
+          score_tiles<Cfg, decltype(ri)::value>(sK, sQ, sP, c, g4, inv_a, EXT, a.log2g);
       });
     }
     __syncthreads();
@@ -801,7 +819,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[qt] = M::step(sa, bq[t & 1][qt], acc[qt]);
       }
-      if constexpr (DEC) {
+      if constexpr (EXT) {
         // the state read out by query i of the chunk is i + 1 steps old
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) acc[qt] *= exp2f(static_cast<float>(16 * qt + c + 1) * a.log2g);
@@ -879,7 +897,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       frag bu[KSC];
 #pragma unroll
       for (int u = 0; u < KSC; ++u) bu[u] = bv[u];
-      if constexpr (DEC) {
+      if constexpr (EXT) {
         const float gs = exp2f(static_cast<float>(nv) * a.log2g);
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) S[ft] *= gs;

@@ -20,7 +20,8 @@ def test_every_declared_function_is_exported():
                           "taylor_feature_map", "taylor_attn_prefill_workspace",
                           "taylor_attn_prefill", "taylor_attn_decode",
                           "taylor_attn_prefill_decayed_workspace", "taylor_attn_prefill_decayed",
-                          "taylor_attn_decode_decayed"}
+                          "taylor_attn_decode_decayed", "taylor_attn_prefill_ext_workspace",
+                          "taylor_attn_prefill_ext", "taylor_attn_decode_ext"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -160,3 +161,25 @@ def test_decayed_entry_points_reject_bad_arguments():
     assert need > 0
     assert pre(0.9, B=2, H=8, N=8192, ws=FAKE, ws_bytes=need - 1) == TAYLOR_ERR_WORKSPACE
     assert L.taylor_attn_prefill_decayed_workspace(1, 1, 64, 16, 64, 2, TAYLOR_BF16) == ctypes.c_size_t(-1).value
+
+
+def test_ext_entry_points_reject_bad_arguments():
+    def pre(ext):
+        return L.taylor_attn_prefill_ext(FAKE, FAKE, FAKE, TAYLOR_BF16, 1, 2, 64, 16, 64, 3, 4.0, ext, None, None,
+                                         FAKE, TAYLOR_BF16, None, None, None, 0, None)
+
+    def dec(ext):
+        return L.taylor_attn_decode_ext(FAKE, FAKE, FAKE, TAYLOR_F32, 2, 3, 16, 64, 3, 4.0, ext, FAKE, FAKE, FAKE,
+                                        TAYLOR_F32, None)
+
+    assert pre(None) == TAYLOR_ERR_NULL_PTR
+    assert dec(None) == TAYLOR_ERR_NULL_PTR
+    for kw in ({"gamma": 0.0}, {"gamma": 2.0}, {"q_scale": 0.0}, {"k_scale": -1.0}, {"q_scale": float("inf")},
+               {"k_scale": float("nan")}):
+        opts = dict(gamma=1.0, qk_norm=1, q_scale=1.0, k_scale=1.0, q_head_scale=None)
+        opts.update(kw)
+        ext = ctypes.byref(tl.Ext(**opts))
+        assert pre(ext) == TAYLOR_ERR_BAD_SCALE, kw
+        assert dec(ext) == TAYLOR_ERR_BAD_SCALE, kw
+    assert (L.taylor_attn_prefill_ext_workspace(2, 8, 8192, 16, 64, 5, TAYLOR_BF16)
+            == L.taylor_attn_prefill_decayed_workspace(2, 8, 8192, 16, 64, 5, TAYLOR_BF16))
