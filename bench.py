@@ -326,6 +326,37 @@ def sweep(args, torch, tl):
           flush=True)
 
 
+def time_workloads(names, torch, tl, W, reps=20):
+    """One prefill call per named workload (its own inputs, output in the input
+    dtype), 3 warm-up and `reps` timed calls; one JSON line per workload."""
+    for name in names:
+        w = W.WORKLOADS[name]
+        x = W.make_workload(w)
+        q, k, v = (dev_tensor(x[s], w.dtype, torch) for s in "qkv")
+        od = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        wsb = tl.prefill_workspace_bytes(w.B, w.H, w.N, w.d, w.dv, w.n_terms, q.dtype)
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        o = torch.empty((w.B, w.H, w.N, w.dv), dtype=od, device="cuda")
+        L = tl.lib()
+        code = tl.TAYLOR_BF16 if w.dtype == "bf16" else tl.TAYLOR_F32
+
+        def step(i):
+            st = L.taylor_attn_prefill(tl._ptr(q), tl._ptr(k), tl._ptr(v), code, w.B, w.H, w.N, w.d, w.dv,
+                                       w.n_terms, w.a, None, None, tl._ptr(o), code, None, None, tl._ptr(ws), wsb,
+                                       tl._stream())
+            if st != 0:
+                tl.check(st)
+
+        for i in range(3):
+            step(i)
+        ms = time_loop(step, reps, torch)
+        _, flops, F = algorithmic_prefill(w)  # both large-feature kernels use 32-token chunks
+        print(json.dumps({"workload": name, "ms": round(ms, 4), "tokens_per_s": w.B * w.N / (ms * 1e-3),
+                          "algorithmic_tflops": flops / (ms * 1e-3) / 1e12, "features": F,
+                          "workspace_MB": wsb / 1e6}), flush=True)
+        del q, k, v, o, ws
+
+
 def cpu_baseline(w, x, budget_s):
     """fp64 oracle direct() on the first heads of the same inputs until ~budget_s."""
     from oracle import taylor_oracle as T
@@ -360,6 +391,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--time", nargs="+", metavar="WORKLOAD",
+                    help="time one prefill call of each named workload, then exit")
     ap.add_argument("--sweep", action="store_true",
                     help="growth of prefill time with N and of decode time with the context, then exit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -382,6 +415,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         sweep(args, torch, tl)
+        return
+    if args.time:
+        time_workloads(args.time, torch, tl, W)
         return
     if args.only == "copy":
         # plain copy of known size, for counter calibration (FETCH_SIZE / WRITE_SIZE)
