@@ -48,6 +48,13 @@ struct PrefillArgs {
   int H;
 };
 
+// Smallest segment count that keeps every segment's rows below 2^31 bytes,
+// the range of a 32-bit buffer resource: rows per segment * row_bytes < 2^31.
+inline int64_t min_segments(int64_t nchunks, int chunk, int64_t row_bytes) {
+  const int64_t max_chunks = (((int64_t{1} << 31) - 1) / row_bytes) / chunk;
+  return (nchunks + max_chunks - 1) / max_chunks;
+}
+
 // Plans a prefill of BH heads x N tokens. Returns false when
 // (d, dv, n_terms, bf16) is not instantiated. `decay` selects the kernel
 // family that supports a decayed state (the generic one).

@@ -328,7 +328,8 @@ __device__ __forceinline__ PairJobs<Cfg> pair_jobs(int tid) {
   return pj;
 }
 template <class Cfg, class KE>
-__device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, float* TQ, KE* TK, bool qside) {
+__device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, float* __restrict__ TQ,
+                                            KE* __restrict__ TK, bool qside) {
   constexpr int D = Cfg::D, C = Cfg::C, NPAIR = PairJobs<Cfg>::NPAIR;
 #pragma unroll
   for (int n = 0; n < PairJobs<Cfg>::N; ++n) {
@@ -341,14 +342,30 @@ __device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, fl
       const f32x4* xi = reinterpret_cast<const f32x4*>(TQ + (1 + pi) * Cfg::TP);
       const f32x4* xj = reinterpret_cast<const f32x4*>(TQ + (1 + pjj) * Cfg::TP);
       f32x4* dst = reinterpret_cast<f32x4*>(TQ + tab_pair<D>(pi, pjj) * Cfg::TP);
+      // all reads of a half row before its writes (same table: no reordering)
 #pragma unroll
-      for (int u = 0; u < C / 4; ++u) dst[u] = xi[u] * xj[u];
+      for (int h = 0; h < C / 4; h += 4) {
+        f32x4 a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a[u] = xi[h + u];
+          b[u] = xj[h + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[h + u] = a[u] * b[u];
+      }
     } else if constexpr (Cfg::KH) {
       const f16x8* xi = reinterpret_cast<const f16x8*>(TK + (1 + pi) * Cfg::TPK);
       const f16x8* xj = reinterpret_cast<const f16x8*>(TK + (1 + pjj) * Cfg::TPK);
       f16x8* dst = reinterpret_cast<f16x8*>(TK + tab_pair<D>(pi, pjj) * Cfg::TPK);
+      f16x8 a[C / 8], b[C / 8];
 #pragma unroll
-      for (int u = 0; u < C / 8; ++u) dst[u] = xi[u] * xj[u];
+      for (int u = 0; u < C / 8; ++u) {
+        a[u] = xi[u];
+        b[u] = xj[u];
+      }
+#pragma unroll
+      for (int u = 0; u < C / 8; ++u) dst[u] = a[u] * b[u];
     } else {
       const f32x4* xi = reinterpret_cast<const f32x4*>(TK + (1 + pi) * Cfg::TPK);
       const f32x4* xj = reinterpret_cast<const f32x4*>(TK + (1 + pjj) * Cfg::TPK);
@@ -361,7 +378,8 @@ __device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, fl
 
 // Query side: phi~(Q) [C x FS], query-major. Key side: u(KS K)^T [FS x C].
 template <class Cfg, bool QSIDE, class TE_, class DE>
-__device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, const TE_* T, DE* dst) {
+__device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, const TE_* __restrict__ T,
+                                        DE* __restrict__ dst) {
   constexpr int NB = (Cfg::FS + 63) / 64, NBW = (NB + Cfg::NW - 1) / Cfg::NW, C = Cfg::C;
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
@@ -369,8 +387,8 @@ __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, cons
     const int fl = 64 * blk + lane;
     if (blk >= NB || fl >= Cfg::FS) continue;
     if constexpr (QSIDE) {
-      const float* ta = T + tf[j].oa;
-      const float* tb = T + tf[j].ob;
+      const float* __restrict__ ta = T + tf[j].oa;
+      const float* __restrict__ tb = T + tf[j].ob;
       const float cf = tf[j].cq;
 #pragma unroll
       for (int t0 = 0; t0 < C; t0 += 4) {
@@ -533,6 +551,14 @@ __device__ __forceinline__ void score_tiles(const typename Cfg::E* sK, const typ
 // the kernel
 // ---------------------------------------------------------------------------
 
+// Raw buffer resource over `bytes` bytes at p (loads past the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
 enum { MODE_SEGSUM = 0, MODE_MAIN = 1 };
 
 template <class Cfg, int MODE, bool EXT>
@@ -671,24 +697,30 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   constexpr int NSLOT = (NIT + Cfg::NTHR - 1) / Cfg::NTHR;
   uint4 pf[NSLOT];
 
+  // Buffer resources over this segment's rows (base and size in scalar
+  // registers): rows past the segment, and Q when no output is wanted, read
+  // as zero without branches.
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  const auto rq = make_rsrc(qh + static_cast<size_t>(t0) * D, want_out ? seg_rows * D * Cfg::ES : 0u);
+  const auto rk = make_rsrc(kh + static_cast<size_t>(t0) * D, seg_rows * D * Cfg::ES);
+  const auto rv = make_rsrc(vh + static_cast<size_t>(t0) * DV, seg_rows * DV * Cfg::ES);
   auto fetch = [&](int cc0) {
-    const int nvv = min(C, t1 - cc0);
+    const uint32_t r0 = static_cast<uint32_t>(cc0 - t0);
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int i = tid + s * Cfg::NTHR;
       pf[s] = uint4{0, 0, 0, 0};
       if (i < QB) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
-        if (want_out && row < nvv)
-          pf[s] = *reinterpret_cast<const uint4*>(qh + static_cast<size_t>(cc0 + row) * D + col);
+        pf[s] = bload16(rq, ((r0 + row) * D + col) * Cfg::ES);
       } else if (i < QB + NQI) {
         const int j = i - QB;
         const int row = j / (D / EV), col = (j % (D / EV)) * EV;
-        if (row < nvv) pf[s] = *reinterpret_cast<const uint4*>(kh + static_cast<size_t>(cc0 + row) * D + col);
+        pf[s] = bload16(rk, ((r0 + row) * D + col) * Cfg::ES);
       } else if (i < NIT) {
         const int j = i - QB - NQI;
         const int row = j / (DV / EV), col = (j % (DV / EV)) * EV;
-        if (row < nvv) pf[s] = *reinterpret_cast<const uint4*>(vh + static_cast<size_t>(cc0 + row) * DV + col);
+        pf[s] = bload16(rv, ((r0 + row) * DV + col) * Cfg::ES);
       }
     }
   };
@@ -754,8 +786,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     const bool do_update = !MAIN || !last_chunk || want_state;
 
     stage(nv);
-    if (!last_chunk) fetch(c0 + C);
     __syncthreads();
+    // next chunk's loads after the barrier: a workgroup barrier waits for
+    // every outstanding global access, so loads issued before it would not
+    // overlap this chunk's work
+    if (!last_chunk) fetch(c0 + C);
 
     // features and score tiles
     if constexpr (Cfg::UNROLL) {
@@ -1132,7 +1167,9 @@ static void plan_cfg(int BH, int N, PrefillPlan* p) {
   const int64_t target = 512;
   const int64_t want = (target + static_cast<int64_t>(BH) * Cfg::G - 1) / (static_cast<int64_t>(BH) * Cfg::G);
   const int64_t maxp = nchunks / 4 > 1 ? nchunks / 4 : 1;
-  const int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
+  int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
+  const int64_t minp = min_segments(nchunks, C, static_cast<int64_t>(Cfg::D > Cfg::DV ? Cfg::D : Cfg::DV) * Cfg::ES);
+  if (P < minp) P = minp;
   const int64_t cps = (nchunks + P - 1) / P;
   p->L = static_cast<int>(cps * C);
   p->P = static_cast<int>((nchunks + cps - 1) / cps);

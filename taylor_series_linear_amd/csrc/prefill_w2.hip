@@ -727,7 +727,9 @@ bool plan(int BH, int N, PrefillPlan* pl) {
   const int64_t target = 256;
   const int64_t want = (target + 2 * BH - 1) / (2 * BH);
   const int64_t maxp = nch / 8 > 1 ? nch / 8 : 1;
-  const int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
+  int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
+  const int64_t minp = min_segments(nch, C, D * 2);  // 32-bit buffer ranges per segment
+  if (P < minp) P = minp;
   const int64_t cps = (nch + P - 1) / P;
   pl->L = static_cast<int>(cps * C);
   pl->P = static_cast<int>((nch + cps - 1) / cps);
