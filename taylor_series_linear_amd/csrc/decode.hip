@@ -15,7 +15,9 @@
 // by HBM bandwidth (about 0.5 flop per state byte), so the kernel is shaped
 // for coalescing: 16 lanes cover one 64-float state row with 16-byte
 // accesses, every lane keeps several rows in flight, and the per-feature
-// weights phi(k), alpha*phi(q) are computed once per head into LDS.
+// weights phi(k), alpha*phi(q) are computed once per head into LDS. State
+// accesses are non-temporal: each byte is touched once per step, and the
+// streaming hint lifts the read-modify-write rate above that of a plain copy.
 #include "features.hpp"
 #include "internal.hpp"
 #include "mma.hpp"
@@ -65,7 +67,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < BATCH; ++j) {
       const int f = rg + NG * (r0 + j);
-      if (r0 + j < RPT && f < F) rows[j] = *reinterpret_cast<const f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq);
+      if (r0 + j < RPT && f < F)
+        rows[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq));
     }
   };
   load_batch(0);
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < ZPT; ++j) {
     const int f = tid + 256 * j;
-    zv[j] = f < F ? zh[f] : 0.f;
+    zv[j] = f < F ? __builtin_nontemporal_load(zh + f) : 0.f;
   }
 
   if (tid < D) {
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const int f = rg + NG * (r0 + j);
       if (r0 + j < RPT && f < F) {
         const f32x4 s = rows[j] * g + sfk[f] * vv;
-        *reinterpret_cast<f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq) = s;
+        __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq));
         acc += sfq[f] * s;
       }
     }
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int f = tid + 256 * j;
     if (f < F) {
       const float zz = zv[j] * g + sfk[f];
-      zh[f] = zz;
+      __builtin_nontemporal_store(zz, zh + f);
       dpart += sfq[f] * zz;
     }
   }
