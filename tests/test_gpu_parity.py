@@ -296,3 +296,57 @@ def test_state_rank_on_gpu_features(d, n):
         assert rank == Fm
         f0 += Fm
     assert f0 == phi.shape[1]
+
+
+def test_state_truncation_breaks_gpu_readout():
+    # "Expanding Attention", "Higher orders": the order-2 state spans all
+    # C(d+1, 2) = 136 key directions at d = 16, and none can be dropped. The
+    # GPU prefill state is read out through the GPU decode step with orders 0
+    # and 1 cleared, so the read-out is the order-2 term alone. Its order-2
+    # block is then rebuilt from the GPU feature map's key features truncated
+    # to r singular directions: at r = 136 the read-out equals the prefill
+    # state's to fp32 rounding, below it the error jumps by orders of magnitude.
+    d, dv, n, a, N, M = 16, 64, 3, 4.0, 512, 8
+    x = _inputs(1, 1, N, d, dv, "f32", 909, qk="unit")
+    k = to_device(x["k"], "f32")
+    v = to_device(x["v"], "f32")
+    _, S, z = tl.prefill(k, k, v, n, a, want_output=False, return_state=True)
+    phi = to_f64(tl.feature_map(k[0, 0].contiguous(), n))
+    lo, hi = 1 + d, T.n_features(d, n)
+    G = phi[:, lo:hi]
+    U, s, Vt = np.linalg.svd(G, full_matrices=False)
+    assert len(s) == math.comb(d + 1, 2)
+    rng = np.random.default_rng(910)
+    qm = rng.standard_normal((M, 1, d))
+    qm /= np.linalg.norm(qm, axis=-1, keepdims=True)
+    qd = torch.tensor(qm, dtype=torch.float32, device="cuda")
+    zero_k = torch.zeros((M, 1, d), dtype=torch.float32, device="cuda")
+    zero_v = torch.zeros((M, 1, dv), dtype=torch.float32, device="cuda")
+
+    def readout(S2, z2):
+        # M copies of the state, orders 0 and 1 cleared; the step's own token
+        # (k = 0, v = 0) adds 1 to z_0, so o = a2 phi_2(q) S_2 / (1 + a2 phi_2(q) z_2)
+        Sx = torch.zeros((M, 1, hi, dv), dtype=torch.float32, device="cuda")
+        zx = torch.zeros((M, 1, hi), dtype=torch.float32, device="cuda")
+        Sx[:, :, lo:hi] = S2
+        zx[:, :, lo:hi] = z2
+        o = tl.decode(qd, zero_k, zero_v, Sx, zx, n, a)
+        torch.cuda.synchronize()
+        return to_f64(o)[:, 0]
+
+    o_state = readout(S[0, 0, lo:hi], z[0, 0, lo:hi])
+    # exact order-2 read-out in fp64 from the same inputs
+    w2 = (qm[:, 0] @ x["k64"][0, 0].T / a) ** 2 / 2
+    exact = (w2 @ x["v64"][0, 0]) / (1 + w2.sum(axis=1))[:, None]
+    say(f"order-2 read-out of the prefill state vs exact: {normwise_rel(o_state, exact, 0):.2e}")
+    assert normwise_rel(o_state, exact, 0) < 1e-4
+    errs = {}
+    for r in (136, 135, 120):
+        Gr = (U[:, :r] * s[:r]) @ Vt[:r]
+        S2 = torch.tensor(Gr.T @ x["v64"][0, 0], dtype=torch.float32, device="cuda")
+        z2 = torch.tensor(Gr.sum(axis=0), dtype=torch.float32, device="cuda")
+        errs[r] = normwise_rel(readout(S2, z2), o_state, 0)
+        say(f"rank {r} of 136: read-out error {errs[r]:.2e}")
+    assert errs[136] < 1e-4
+    assert errs[135] > 100 * errs[136] and errs[135] > 1e-2
+    assert errs[120] > errs[135]
