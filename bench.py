@@ -13,7 +13,7 @@ heads, states seeded by a 32768-token prefill) as a fraction of HBM peak, the
 roofline of the dominant kernel and the fp64 CPU oracle timed beside it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--no-decode] [--only prefill|decode|copy]
+       [--no-decode] [--no-native] [--only prefill|decode|copy]
 """
 from __future__ import annotations
 
@@ -243,6 +243,25 @@ def bench_decode(args, torch, tl, W):
     }
 
 
+def native_c_abi():
+    """Decode and prefill timed through the C ABI by a plain C++ host program
+    (taylor_series_linear_amd/bench_native, built with the library), run as a
+    child process with no Python or torch in it: a cross-check of the figures
+    above with the library used the way a C or C++ caller would use it."""
+    import subprocess
+    exe = os.path.join(ROOT, "taylor_series_linear_amd", "bench_native")
+    if not os.path.exists(exe):
+        return {"skipped": "bench_native is not built"}
+    log("native: timing decode and prefill through the C ABI in a child process")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        raise SystemExit(f"bench_native failed ({r.returncode}): {r.stderr.strip()}")
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    res["note"] = ("same kernels and workloads, timed by HIP events in a C++ process; decode states seeded by a "
+                   "256-token prefill (the state size does not depend on the context length)")
+    return res
+
+
 def _fit_exponent(ns, ts):
     """Least-squares slope of log t against log N."""
     x = np.log(np.asarray(ns, dtype=np.float64))
@@ -398,6 +417,7 @@ def main():
     ap.add_argument("--decode-replicas", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-native", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
     ap.add_argument("--time", nargs="+", metavar="WORKLOAD",
@@ -473,6 +493,8 @@ def main():
     }
     if args.only != "prefill" and not args.no_decode:
         out["decode"] = bench_decode(args, torch, tl, W)
+    if not args.no_native and args.only is None:
+        out["native_c_abi"] = native_c_abi()
     if not args.no_cpu and args.only is None:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(out))

@@ -17,6 +17,10 @@ BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.hip", "prefill.hip", "prefill_o2.hip", "prefill_w2.hip", "decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+# host program timing the C ABI without Python (bench.py runs it as a child process)
+NATIVE_SRC = os.path.join(CSRC, "bench_native.cpp")
+NATIVE_EXE = os.path.join(HERE, "bench_native")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # keep the compiler from forming packed fp32 instructions
@@ -47,6 +51,13 @@ def build(jobs: int = 4) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, OUT)
+    cmd = [HIPCC, "-O2", "-std=c++17", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include"),
+           "-x", "c++", NATIVE_SRC, "-o", NATIVE_EXE + ".tmp", "-L" + HERE, "-ltaylor_attn",
+           "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("bench_native build failed:\n" + r.stderr)
+    os.replace(NATIVE_EXE + ".tmp", NATIVE_EXE)
     return OUT
 
 
