@@ -259,8 +259,11 @@ struct Smem {
 // ---------------------------------------------------------------------------
 
 // Sync area of the single-pass launch (ints): one flag per (head, segment),
-// then the work-ticket counter. o2_reset clears it at the start of a call.
+// then the work-ticket counter and one counter per workgroup group.
+// o2_reset clears it at the start of a call.
+constexpr int kGroups = 8;
 __host__ __device__ constexpr int sync_ints(int units) { return units + 64; }
+static_assert(1 + kGroups <= 64, "group counters fit the sync area");
 
 __global__ __launch_bounds__(256) void o2_reset(int* sync, int n) {
   for (int i = threadIdx.x; i < n; i += 256) sync[i] = 0;
@@ -290,8 +293,22 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   // Work unit. With several segments the unit comes from a ticket counter,
   // so tickets follow dispatch order: a workgroup only ever waits for
   // segments of lower tickets, whose workgroups are already running and
-  // publish their sums without waiting themselves.
-  if (tid == 0) s_unit = P > 1 ? atomicAdd(flags + units, 1) : static_cast<int>(blockIdx.x);
+  // publish their sums without waiting themselves. When the heads split
+  // evenly, workgroups are grouped by blockIdx % 8 (the XCD a workgroup
+  // is dispatched to) with one counter per group, and group g serves heads
+  // g, g + 8, ...: all segments of a head then share one XCD, and the
+  // ticket argument holds within each group.
+  if (tid == 0) {
+    if (P == 1) {
+      s_unit = static_cast<int>(blockIdx.x);
+    } else if (a.BH % kGroups == 0) {
+      const int g = static_cast<int>(blockIdx.x % kGroups);
+      const int t = atomicAdd(flags + units + 1 + g, 1);
+      s_unit = ((t / P) * kGroups + g) * P + t % P;
+    } else {
+      s_unit = atomicAdd(flags + units, 1);
+    }
+  }
   __syncthreads();
   const int unit = __builtin_amdgcn_readfirstlane(s_unit);
   if (unit >= units) return;
@@ -768,21 +785,7 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
     if (!want_out) return;
   }
 
-  // constant parts of both phase-3 buffers: Q' columns 16..31 = (1, 0, ...);
-  // K'^T row 17 = 0.
-  for (int i = tid; i < 2 * C * 16; i += NTHR) {
-    const int b = i / (C * 16), rest = i % (C * 16), row = rest / 16, col = 16 + rest % 16;
-    sm.qp(b)[row * QP_P + col] = static_cast<__bf16>(col == 16 ? 1.f : 0.f);
-  }
-  for (int i = tid; i < 2 * KF_P; i += NTHR) sm.kt(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
-
   // phase 2: initial state = S0 + the sums of segments 0..p-1 ---------------
-  if (w < 2) {
-#pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) S[ft] = f32x16{};
-  } else if (w == 2) {
-    Z = f32x16{};
-  }
   if (p > 0 && tid == 0) {
     // The wait is bounded (about a second) so that a broken invariant shows
     // as wrong output rather than a workgroup that never ends.
@@ -793,25 +796,66 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
         __builtin_amdgcn_s_sleep(2);
   }
   __syncthreads();
-  for (int q = 0; q < p; ++q) {
-    const auto ru = make_rsrc(unit_ptr(q), static_cast<uint32_t>(UNIT_BYTES));
+  if (p == 0) {
+    if (w < 2) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft) S[ft] = f32x16{};
+    } else if (w == 2) {
+      Z = f32x16{};
+    }
+  } else {
+    // All four waves add up the earlier sums: wave w takes float4 items
+    // [w RQ, (w+1) RQ) of every sum, with two sums' loads in flight at a
+    // time, and leaves the total in LDS (free until phase 3) in the unit
+    // layout, from which the owning waves read their accumulators.
+    constexpr int RQ = UNIT_F4 / 4;
+    constexpr int RJ = RQ / 64;
+    static_assert(RQ % 64 == 0 && UNIT_BYTES <= static_cast<size_t>(lds_bytes<true>()) &&
+                      UNIT_BYTES <= static_cast<size_t>(lds_bytes<false>()),
+                  "whole float4 items per lane; the total fits the kernel's LDS");
+    f32x4 acc[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int i0 = w * RQ + l;
+    int q = 0;
+    for (; q + 2 <= p; q += 2) {
+      const auto r0 = make_rsrc(unit_ptr(q), static_cast<uint32_t>(UNIT_BYTES));
+      const auto r1 = make_rsrc(unit_ptr(q + 1), static_cast<uint32_t>(UNIT_BYTES));
+      f32x4 x0[RJ], x1[RJ];
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) x0[j] = ld_dev(r0, i0 + 64 * j);
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) x1[j] = ld_dev(r1, i0 + 64 * j);
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) acc[j] += x0[j] + x1[j];
+    }
+    if (q < p) {
+      const auto r0 = make_rsrc(unit_ptr(q), static_cast<uint32_t>(UNIT_BYTES));
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) acc[j] += ld_dev(r0, i0 + 64 * j);
+    }
+    f32x4* const tot = reinterpret_cast<f32x4*>(smem_raw);
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) tot[i0 + 64 * j] = acc[j];
+    __syncthreads();
     if (w < 2) {
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 x = ld_dev(ru, unit_idx(w, ft, q4));
+          const f32x4 x = tot[unit_idx(w, ft, q4)];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) S[ft][4 * q4 + r] += x[r];
+          for (int r = 0; r < 4; ++r) S[ft][4 * q4 + r] = x[r];
         }
     } else if (w == 2) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 x = ld_dev(ru, ZIDX + q4 * 64 + l);
+        const f32x4 x = tot[ZIDX + q4 * 64 + l];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Z[4 * q4 + r] += x[r];
+        for (int r = 0; r < 4; ++r) Z[4 * q4 + r] = x[r];
       }
     }
+    __syncthreads();  // the area is reused below
   }
   if (w < 2 && a.S0 != nullptr) {
     const int col = 32 * w + lc;
@@ -839,6 +883,15 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       Z[j] += x;
     }
   }
+
+  // constant parts of both phase-3 buffers: Q' columns 16..31 = (1, 0, ...);
+  // K'^T row 17 = 0.
+  for (int i = tid; i < 2 * C * 16; i += NTHR) {
+    const int b = i / (C * 16), rest = i % (C * 16), row = rest / 16, col = 16 + rest % 16;
+    sm.qp(b)[row * QP_P + col] = static_cast<__bf16>(col == 16 ? 1.f : 0.f);
+  }
+  for (int i = tid; i < 2 * KF_P; i += NTHR) sm.kt(i / KF_P)[17 * KF_P + i % KF_P] = static_cast<_Float16>(0.f);
+  __syncthreads();  // the K wave reads row 17 while building chunk 0
 
   // phase 3: outputs (and, for the last segment, the final state) -----------
   pass(std::true_type{});
