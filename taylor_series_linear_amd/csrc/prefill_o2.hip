@@ -259,11 +259,14 @@ struct Smem {
 // ---------------------------------------------------------------------------
 
 // Sync area of the single-pass launch (ints): one flag per (head, segment),
-// then the work-ticket counter and one counter per workgroup group.
-// o2_reset clears it at the start of a call.
+// then the work-ticket counter and one counter per workgroup group, each
+// counter in a 128-byte line of its own: every workgroup of a call takes a
+// ticket at its start, and atomics on one line are served one at a time.
+// o2_reset clears the area at the start of a call.
 constexpr int kGroups = 8;
-__host__ __device__ constexpr int sync_ints(int units) { return units + 64; }
-static_assert(1 + kGroups <= 64, "group counters fit the sync area");
+constexpr int kCtrStride = 32;  // ints per counter line
+__host__ __device__ constexpr int ctr_base(int units) { return (units + kCtrStride - 1) / kCtrStride * kCtrStride; }
+__host__ __device__ constexpr int sync_ints(int units) { return ctr_base(units) + kCtrStride * (kGroups + 1); }
 
 __global__ __launch_bounds__(256) void o2_reset(int* sync, int n) {
   for (int i = threadIdx.x; i < n; i += 256) sync[i] = 0;
@@ -303,10 +306,10 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       s_unit = static_cast<int>(blockIdx.x);
     } else if (a.BH % kGroups == 0) {
       const int g = static_cast<int>(blockIdx.x % kGroups);
-      const int t = atomicAdd(flags + units + 1 + g, 1);
+      const int t = atomicAdd(flags + ctr_base(units) + kCtrStride * (1 + g), 1);
       s_unit = ((t / P) * kGroups + g) * P + t % P;
     } else {
-      s_unit = atomicAdd(flags + units, 1);
+      s_unit = atomicAdd(flags + ctr_base(units), 1);
     }
   }
   __syncthreads();
