@@ -789,14 +789,21 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   }
 
   // phase 2: initial state = S0 + the sums of segments 0..p-1 ---------------
-  if (p > 0 && tid == 0) {
-    // The wait is bounded (about a second) so that a broken invariant shows
-    // as wrong output rather than a workgroup that never ends.
+  if (p > 0 && tid < 64) {
+    // The first 64 threads poll up to 64 flags at once (one device-scope
+    // load each; a flag read costs a memory round trip) until a wave vote
+    // finds them all set. The wait is bounded (about a second) so that a
+    // broken invariant shows as wrong output rather than a workgroup that
+    // never ends.
     int spins = 0;
-    for (int q = 0; q < p; ++q)
-      while (__hip_atomic_load(flags + bh * P + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 &&
-             ++spins < (1 << 24))
+    for (int q0 = 0; q0 < p; q0 += 64) {
+      const int q = q0 + tid;
+      while (true) {
+        const int f = q < p ? __hip_atomic_load(flags + bh * P + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
+        if (__all(f != 0) || ++spins >= (1 << 20)) break;
         __builtin_amdgcn_s_sleep(2);
+      }
+    }
   }
   __syncthreads();
   if (p == 0) {
