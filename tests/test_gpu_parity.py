@@ -105,6 +105,27 @@ def test_prefill_multi_segment(d, dv, n, dtype):
     assert normwise_rel(to_f64(S), Sr) < TOL[dtype]
 
 
+@pytest.mark.parametrize("B,H", [(1, 8), (2, 8), (3, 5)])
+def test_order2_prefill_head_groups(B, H):
+    # The order-2 d=16 bf16 kernel splits each head into segments and, when
+    # B*H is a multiple of 8, hands out work per group of workgroups (one
+    # ticket counter per blockIdx % 8); 3 x 5 heads take the single-counter
+    # path. Every row and the final state are checked against the oracle, on
+    # a ragged length that leaves a partial last chunk.
+    N, d, dv, n = 1100, 16, 64, 3
+    a = math.sqrt(d)
+    x = _inputs(B, H, N, d, dv, "bf16", 4100 + 10 * B + H)
+    say("order-2 head groups", B, H)
+    o, S, z = _run_prefill(x, n, a, "bf16", out_dtype=torch.float32, return_state=True)
+    ref = T.direct(x["q64"], x["k64"], x["v64"], n, a)
+    err = normwise_rel(to_f64(o), ref)
+    say("  err", err)
+    assert err < TOL["bf16"]
+    Sr, zr = T.state(x["k64"], x["v64"], n)
+    assert normwise_rel(to_f64(S), Sr) < TOL["bf16"]
+    assert normwise_rel(to_f64(z)[..., None], zr[..., None]) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("inplace", [False, True])
 @pytest.mark.parametrize("N1,N2", [(100, 37), (1500, 2100)])
