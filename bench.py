@@ -253,10 +253,17 @@ def native_c_abi():
     if not os.path.exists(exe):
         return {"skipped": "bench_native is not built"}
     log("native: timing decode and prefill through the C ABI in a child process")
-    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    # a failure here is reported in this block and never stops the bench line
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    except subprocess.TimeoutExpired:
+        return {"error": "bench_native did not finish within 300 s"}
     if r.returncode != 0:
-        raise SystemExit(f"bench_native failed ({r.returncode}): {r.stderr.strip()}")
-    res = json.loads(r.stdout.strip().splitlines()[-1])
+        return {"error": f"bench_native exited with {r.returncode}: {r.stderr.strip()[-500:]}"}
+    try:
+        res = json.loads(r.stdout.strip().splitlines()[-1])
+    except (ValueError, IndexError):
+        return {"error": "bench_native printed no JSON line"}
     res["note"] = ("same kernels and workloads, timed by HIP events in a C++ process; decode states seeded by a "
                    "256-token prefill (the state size does not depend on the context length)")
     return res
