@@ -185,6 +185,8 @@ __device__ __forceinline__ float zscale(int r, int c, float inv_a) {
 // ---------------------------------------------------------------------------
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma32h(f16x8 a, f16x8 b, f32x16 c) {
@@ -491,6 +493,18 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
 
   // M wave: one chunk from buffer b. OUT: read out and store the chunk's
   // outputs; UPD: fold the chunk into S.
+  // M wave: constants of the intra-chunk weights, evaluated two at a time in
+  // fp16 (the precision P has in its MFMA): 1/a, and per lane the causal mask
+  // of accumulator elements 2j, 2j + 1 as 0/1 factors (key after query: 0).
+  const f16x2 one_h = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  const f16x2 half_h = {static_cast<_Float16>(0.5f), static_cast<_Float16>(0.5f)};
+  const f16x2 inva_h = {static_cast<_Float16>(inv_a), static_cast<_Float16>(inv_a)};
+  f16x2 cmask[8];
+#pragma unroll
+  for (int j2 = 0; j2 < 8; ++j2)
+    cmask[j2] = f16x2{static_cast<_Float16>(acc_row(2 * j2, lh) > lc ? 0.f : 1.f),
+                      static_cast<_Float16>(acc_row(2 * j2 + 1, lh) > lc ? 0.f : 1.f)};
+
   auto m_chunk = [&](int i, bool out, bool upd) __attribute__((always_inline)) {
     const int b = i & 1;
     const int m = w;
@@ -499,21 +513,24 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       const bf16x8 kf = ld8(sm.kr(b) + lc * K_P + 8 * lh);
       const bf16x8 qf = ld8(sm.qp(b) + lc * QP_P + 8 * lh);
       const f32x16 sc = mfma32(kf, qf, f32x16{});
+      // weights 1 + t + t^2/2 of t = y/a for the raw scores y = q.k, two per
+      // packed fp16 instruction, masked; the denominator sums the same fp16
+      // weights the P V product uses, in fp32
       f16x8 P0, P1;
       float den = 0.f;
-      const float c2 = 0.5f * inv_a * inv_a;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = acc_row(j, lh);
-        // 1 + y/a + y^2/(2a^2) for the raw score y = q.k
-        float wv = __builtin_fmaf(__builtin_fmaf(c2, sc[j], inv_a), sc[j], 1.f);
-        if (key > lc) wv = 0.f;  // causal mask (key after query)
-        const _Float16 pb = static_cast<_Float16>(wv);
-        den += wv;
-        if (j < 8)
-          P0[j] = pb;
-        else
-          P1[j - 8] = pb;
+      for (int j2 = 0; j2 < 8; ++j2) {
+        const f16x2 t = __builtin_convertvector(f32x2{sc[2 * j2], sc[2 * j2 + 1]}, f16x2) * inva_h;
+        const f16x2 wv =
+            __builtin_elementwise_fma(__builtin_elementwise_fma(half_h, t, one_h), t, one_h) * cmask[j2];
+        den = __builtin_amdgcn_fdot2(wv, one_h, den, false);
+        if (j2 < 4) {
+          P0[2 * j2] = wv[0];
+          P0[2 * j2 + 1] = wv[1];
+        } else {
+          P1[2 * j2 - 8] = wv[0];
+          P1[2 * j2 - 7] = wv[1];
+        }
       }
       // read-out: O^T[dv][query] = S^T phi~(Q)^T over 10 k-steps
       f32x16 O = f32x16{};
