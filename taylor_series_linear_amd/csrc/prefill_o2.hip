@@ -27,8 +27,8 @@
 // z_1 = Z[i][16], z_2 = Z[i][j]. The read-out q'^T Z~ q' with q' = [q, 1]
 // and Z~ = Z scaled by 1/(2a^2), 1/(2a), 1 on its blocks equals
 // sum_m alpha_m phi_m(q).z_m. Z is 32x32 in the MFMA (rows/cols 17..31 are
-// zero) and its read-out uses a hi/lo bf16 split so the count z_0 is not
-// rounded to 8 bits.
+// zero). Its read-out adds the count z_0 in fp32, outside the bf16
+// contraction of the other entries, so the count is not rounded to 8 bits.
 //
 // Precision: scores and the read-out use bf16 operands; the state update,
 // the intra-chunk term and Z use fp16 operands (keys, values, key products
@@ -462,22 +462,25 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   };
 
   // Q wave: inter-chunk denominator of the queries in buffer b from Z.
+  // The count of earlier keys, Z[16][16] (weight 1), stays outside the bf16
+  // contraction: lane 16 holds it in element 8 (row acc_row(8, 0) = 16), in
+  // fp32 and exact; every other entry of Z~ is rounded to bf16 once, as the
+  // state is in the read-out.
   auto den_inter = [&](int b) __attribute__((always_inline)) {
+    const float z00 = __shfl(Z[8], 16);
     f32x16 dq = f32x16{};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      bf16x8 hi, lo;
+      bf16x8 hi;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int j = 8 * u + s;
         const float x = Z[j] * zscale(lc, acc_row(j, lh), inv_a);
-        hi[s] = static_cast<__bf16>(x);
-        lo[s] = static_cast<__bf16>(x - static_cast<float>(hi[s]));
+        hi[s] = static_cast<__bf16>(j == 8 && l == 16 ? 0.f : x);
       }
       const __bf16* qrow = sm.qp(b) + lc * QP_P;
       const bf16x8 bq = cat44(ld4(qrow + 16 * u + 4 * lh), ld4(qrow + 16 * u + 8 + 4 * lh));
       dq = mfma32(hi, bq, dq);
-      dq = mfma32(lo, bq, dq);
     }
     const __bf16* qrow = sm.qp(b) + lc * QP_P;
     float part = 0.f;
@@ -488,11 +491,9 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       for (int r = 0; r < 4; ++r) part += dq[4 * bb + r] * static_cast<float>(qv[r]);
     }
     part += __shfl_xor(part, 32);
-    if (lh == 0) sm.den(b)[lc] = part;
+    if (lh == 0) sm.den(b)[lc] = part + z00;
   };
 
-  // M wave: one chunk from buffer b. OUT: read out and store the chunk's
-  // outputs; UPD: fold the chunk into S.
   // M wave: constants of the intra-chunk weights, evaluated two at a time in
   // fp16 (the precision P has in its MFMA): 1/a, and per lane the causal mask
   // of accumulator elements 2j, 2j + 1 as 0/1 factors (key after query: 0).
@@ -505,6 +506,8 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
     cmask[j2] = f16x2{static_cast<_Float16>(acc_row(2 * j2, lh) > lc ? 0.f : 1.f),
                       static_cast<_Float16>(acc_row(2 * j2 + 1, lh) > lc ? 0.f : 1.f)};
 
+  // M wave: one chunk from buffer b. OUT: read out and store the chunk's
+  // outputs; UPD: fold the chunk into S.
   auto m_chunk = [&](int i, bool out, bool upd) __attribute__((always_inline)) {
     const int b = i & 1;
     const int m = w;
