@@ -124,14 +124,28 @@ size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_t
  * B, H or N may be 0: then no token is processed; with N = 0 the final state
  * is S0 (or zero). The normalisation divides by a sum of weights that is
  * >= 1/2 per key for n_terms = 3 (>= 0.27 for 5), so it never divides by 0.
- * Range: several bf16 instantiations carry key-side products in fp16 inside
- * the state update (fp32 accumulation): order 2 with d = 16 and dv = 64 (keys,
- * values, k_i k_j and the weights w(q.k/a), also in its intra-chunk term) and
- * d = 64 (k_i k_j and values) need those below 65504; the other bf16
- * instantiations with n_terms > 1 and d > 16 or n_terms = 5 use keys halved,
- * so the products of m halved coordinates (m <= 4) must stay below 65504,
- * e.g. |k_i| < 32 for n_terms = 5. Under the normalisation the method asks
- * for (|q.k/a| of order 1) these always hold.
+ * Range: several bf16 instantiations carry operands in fp16 (largest finite
+ * magnitude 65504) with fp32 accumulation:
+ *  - order 2, d = 16, dv = 64: keys, values, key products k_i k_j, and the
+ *    intra-chunk weights w(q.k/a) (t = q.k/a is formed in fp32, so this
+ *    holds for |t| up to about 360, whatever a is);
+ *  - order 2, d = 64: q/a, the query products q_i q_j / a^2, k_i k_j, values
+ *    and the intra-chunk weights;
+ *  - the other bf16 instantiations with n_terms > 1 and d > 16, or
+ *    n_terms = 5, use keys halved, so the products of m halved coordinates
+ *    (m <= 4) must stay below 65504, e.g. |k_i| < 32 for n_terms = 5.
+ * Under the normalisation the method asks for (|q.k/a| of order 1) these
+ * always hold. Beyond them results are inf or NaN from the first affected
+ * row on; rows of earlier queries stay exact, because the causal mask sets
+ * masked weights to exactly zero.
+ * Long sequences are split into segments that run concurrently; in the
+ * order-2, d = 16, dv = 64 bf16 instantiation a segment waits (boundedly,
+ * about a second) for the sums of the earlier segments of its head. If that
+ * wait ever times out, the segment's output rows, and for the last segment
+ * the final state, are written as NaN rather than silently wrong; the status
+ * is still TAYLOR_OK, since kernels run after the call returns. The
+ * environment variable TAYLOR_ATTN_WAIT_SPINS (read once per process; polls,
+ * default 2^20) lowers the bound, so tests can force that path.
  */
 taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   taylor_dtype in_dtype, int B, int H, int N, int d, int dv,

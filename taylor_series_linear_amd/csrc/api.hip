@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "features.hpp"
@@ -87,6 +88,22 @@ int64_t checked_mul(std::initializer_list<int64_t> xs) {
     r *= x;
   }
   return r;
+}
+
+// Bound of the single-pass order-2 kernel's wait for earlier segments, in
+// polls (about a second by default). TAYLOR_ATTN_WAIT_SPINS overrides it, read
+// once per process: a tiny value lets a test force the timed-out path (the
+// unit's rows and final state come out NaN) without any kernel hanging.
+int wait_spins() {
+  static const int v = [] {
+    const char* e = std::getenv("TAYLOR_ATTN_WAIT_SPINS");
+    if (e != nullptr) {
+      const long x = std::strtol(e, nullptr, 10);
+      if (x >= 1 && x <= (1L << 30)) return static_cast<int>(x);
+    }
+    return 1 << 20;
+  }();
+  return v;
 }
 
 taylor_status hip_status(hipError_t e, const char* where) {
@@ -213,6 +230,7 @@ taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_d
   args.P = p.P;
   args.L = p.L;
   args.inv_a = 1.0f / a;
+  args.wait_spins = wait_spins();
   // In-place continuation with several segments: the first segment reads S0
   // while the last one finishes the state, so the final state goes through
   // the workspace and is copied out afterwards.

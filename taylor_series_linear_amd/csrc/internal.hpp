@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sched.hpp"
+
 namespace tl {
 
 // Sequence split and workspace layout of one prefill call.
@@ -32,6 +34,7 @@ struct PrefillArgs {
   float* fin;   // final-state staging for in-place continuation (defer_state)
   float* part;  // partial outputs of feature-sliced kernels
   int* sync;    // flags and work tickets of single-pass kernels (cleared by the launch)
+  int wait_spins;  // bound of a single-pass kernel's wait for earlier segments (polls)
   int BH;
   int N;
   int P;        // segments per head
@@ -47,13 +50,6 @@ struct PrefillArgs {
   const float* q_head_scale;  // device [H] or null
   int H;
 };
-
-// Smallest segment count that keeps every segment's rows below 2^31 bytes,
-// the range of a 32-bit buffer resource: rows per segment * row_bytes < 2^31.
-inline int64_t min_segments(int64_t nchunks, int chunk, int64_t row_bytes) {
-  const int64_t max_chunks = (((int64_t{1} << 31) - 1) / row_bytes) / chunk;
-  return (nchunks + max_chunks - 1) / max_chunks;
-}
 
 // Plans a prefill of BH heads x N tokens. Returns false when
 // (d, dv, n_terms, bf16) is not instantiated. `decay` selects the kernel

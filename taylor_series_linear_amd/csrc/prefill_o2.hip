@@ -45,10 +45,18 @@
 //    with packed fp16 products.
 // The Q and K waves prepare chunk c+1 in one LDS buffer while the M waves
 // consume chunk c from the other; one barrier per chunk. Global loads run
-// PD chunks ahead in registers. Segments of a head are independent given
-// the sum of the earlier segments' states (additivity, closing paragraph of
-// the same page): a first launch computes per-segment sums, a second turns
-// them into inclusive prefixes, the main launch reads one prefix each.
+// PD chunks ahead in registers.
+//
+// Segments, in one launch. Segments of a head are independent given the sum
+// of the earlier segments' states (additivity, closing paragraph of the same
+// page). Each workgroup takes a work ticket from an atomic counter (tickets
+// follow dispatch order), so it only ever waits for segments of lower
+// tickets, whose workgroups are already running. Unless it holds the head's
+// last segment it first sums its own segment (phase 1), publishes the sum
+// with device-scope stores and sets a flag; it then waits for the flags of
+// the head's earlier segments, adds their published sums and S0 (phase 2),
+// and runs the output pass over its segment (phase 3). The wait is bounded;
+// a timed-out wait makes the unit's outputs and final state NaN.
 #include "internal.hpp"
 #include "mma.hpp"
 
@@ -265,7 +273,7 @@ struct Smem {
 // counter in a 128-byte line of its own: every workgroup of a call takes a
 // ticket at its start, and atomics on one line are served one at a time.
 // o2_reset clears the area at the start of a call.
-constexpr int kGroups = 8;
+constexpr int kGroups = o2s::kGroups;
 constexpr int kCtrStride = 32;  // ints per counter line
 __host__ __device__ constexpr int ctr_base(int units) { return (units + kCtrStride - 1) / kCtrStride * kCtrStride; }
 __host__ __device__ constexpr int sync_ints(int units) { return ctr_base(units) + kCtrStride * (kGroups + 1); }
@@ -278,6 +286,7 @@ template <bool OBF>
 __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem_raw[lds_bytes<OBF>()];
   __shared__ int s_unit;
+  __shared__ int s_wait_failed;
   const Smem sm{smem_raw};
   constexpr int OP = OStage<OBF>::P;
   constexpr int OB = OStage<OBF>::BYTES;
@@ -304,12 +313,13 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   // g, g + 8, ...: all segments of a head then share one XCD, and the
   // ticket argument holds within each group.
   if (tid == 0) {
+    s_wait_failed = 0;
     if (P == 1) {
       s_unit = static_cast<int>(blockIdx.x);
-    } else if (a.BH % kGroups == 0) {
+    } else if (o2s::grouped(a.BH, P)) {
       const int g = static_cast<int>(blockIdx.x % kGroups);
       const int t = atomicAdd(flags + ctr_base(units) + kCtrStride * (1 + g), 1);
-      s_unit = ((t / P) * kGroups + g) * P + t % P;
+      s_unit = o2s::ticket_unit(t, g, P);
     } else {
       s_unit = atomicAdd(flags + ctr_base(units), 1);
     }
@@ -495,16 +505,17 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   };
 
   // M wave: constants of the intra-chunk weights, evaluated two at a time in
-  // fp16 (the precision P has in its MFMA): 1/a, and per lane the causal mask
-  // of accumulator elements 2j, 2j + 1 as 0/1 factors (key after query: 0).
+  // packed fp16 (the precision P has in its MFMA), and per lane the causal
+  // mask of accumulator elements 2j, 2j + 1 as a bit mask of the packed pair
+  // (key after query: all bits clear). The mask is applied with a bitwise
+  // AND, so a masked weight is exactly 0 even where the weight itself would
+  // overflow fp16 (a multiply by 0 would turn inf into NaN).
   const f16x2 one_h = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
   const f16x2 half_h = {static_cast<_Float16>(0.5f), static_cast<_Float16>(0.5f)};
-  const f16x2 inva_h = {static_cast<_Float16>(inv_a), static_cast<_Float16>(inv_a)};
-  f16x2 cmask[8];
+  uint32_t cmask[8];
 #pragma unroll
   for (int j2 = 0; j2 < 8; ++j2)
-    cmask[j2] = f16x2{static_cast<_Float16>(acc_row(2 * j2, lh) > lc ? 0.f : 1.f),
-                      static_cast<_Float16>(acc_row(2 * j2 + 1, lh) > lc ? 0.f : 1.f)};
+    cmask[j2] = (acc_row(2 * j2, lh) > lc ? 0u : 0xFFFFu) | (acc_row(2 * j2 + 1, lh) > lc ? 0u : 0xFFFF0000u);
 
   // M wave: one chunk from buffer b. OUT: read out and store the chunk's
   // outputs; UPD: fold the chunk into S.
@@ -516,16 +527,20 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
       const bf16x8 kf = ld8(sm.kr(b) + lc * K_P + 8 * lh);
       const bf16x8 qf = ld8(sm.qp(b) + lc * QP_P + 8 * lh);
       const f32x16 sc = mfma32(kf, qf, f32x16{});
-      // weights 1 + t + t^2/2 of t = y/a for the raw scores y = q.k, two per
-      // packed fp16 instruction, masked; the denominator sums the same fp16
-      // weights the P V product uses, in fp32
+      // weights 1 + t + t^2/2 of t = y/a for the raw scores y = q.k: t is
+      // formed in fp32 (so any y whose t fits fp16 is fine, and 1/a is not
+      // rounded), then the polynomial runs two per packed fp16 instruction;
+      // the denominator sums the same fp16 weights the P V product uses, in
+      // fp32
       f16x8 P0, P1;
       float den = 0.f;
 #pragma unroll
       for (int j2 = 0; j2 < 8; ++j2) {
-        const f16x2 t = __builtin_convertvector(f32x2{sc[2 * j2], sc[2 * j2 + 1]}, f16x2) * inva_h;
-        const f16x2 wv =
-            __builtin_elementwise_fma(__builtin_elementwise_fma(half_h, t, one_h), t, one_h) * cmask[j2];
+        const f16x2 t = __builtin_convertvector(f32x2{sc[2 * j2] * inv_a, sc[2 * j2 + 1] * inv_a}, f16x2);
+        const f16x2 wv = __builtin_bit_cast(
+            f16x2, __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_elementwise_fma(half_h, t, one_h),
+                                                                          t, one_h)) &
+                       cmask[j2]);
         den = __builtin_amdgcn_fdot2(wv, one_h, den, false);
         if (j2 < 4) {
           P0[2 * j2] = wv[0];
@@ -812,18 +827,26 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
   if (p > 0 && tid < 64) {
     // The first 64 threads poll up to 64 flags at once (one device-scope
     // load each; a flag read costs a memory round trip) until a wave vote
-    // finds them all set. The wait is bounded (about a second) so that a
-    // broken invariant shows as wrong output rather than a workgroup that
-    // never ends.
+    // finds them all set. The wait is bounded (about a second): if it ends
+    // with a flag still clear, the unit's initial state is set to NaN below,
+    // so every output row of the unit (and, for the last segment, the final
+    // state) comes out NaN instead of silently wrong, and the workgroup
+    // still ends.
     int spins = 0;
+    bool all_set = true;
     for (int q0 = 0; q0 < p; q0 += 64) {
       const int q = q0 + tid;
       while (true) {
         const int f = q < p ? __hip_atomic_load(flags + bh * P + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1;
-        if (__all(f != 0) || ++spins >= (1 << 20)) break;
+        if (__all(f != 0)) break;
+        if (++spins >= a.wait_spins) {
+          all_set = false;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
     }
+    if (tid == 0) s_wait_failed = all_set ? 0 : 1;
   }
   __syncthreads();
   if (p == 0) {
@@ -911,6 +934,20 @@ __global__ __launch_bounds__(NTHR, 2) void o2_kernel(PrefillArgs a) {
         x = z0[0];
       }
       Z[j] += x;
+    }
+  }
+
+  // a timed-out wait poisons the unit (see the wait above)
+  if (s_wait_failed) {
+    const float nan = __builtin_nanf("");
+    if (w < 2) {
+#pragma unroll
+      for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) S[ft][j] = nan;
+    } else if (w == 2) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) Z[j] = nan;
     }
   }
 
@@ -1004,22 +1041,12 @@ __global__ __launch_bounds__(192) void o2_state_store(const float4* fin, float* 
 
 bool plan(int BH, int N, PrefillPlan* pl) {
   *pl = PrefillPlan{};
-  const int64_t nch = (static_cast<int64_t>(N) + C - 1) / C;
-  if (BH <= 0 || nch == 0) {
-    pl->P = 1;
-    pl->L = N;
-    return true;
-  }
-  // about two workgroups per compute unit, at least 8 chunks per segment
-  const int64_t target = 512;
-  const int64_t want = (target + BH - 1) / BH;
-  const int64_t maxp = nch / 8 > 1 ? nch / 8 : 1;
-  int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
-  const int64_t minp = min_segments(nch, C, DV * 2);  // 32-bit buffer ranges per segment
-  if (P < minp) P = minp;
-  const int64_t cps = (nch + P - 1) / P;
-  pl->L = static_cast<int>(cps * C);
-  pl->P = static_cast<int>((nch + cps - 1) / cps);
+  // about two workgroups per compute unit, at least 8 chunks per segment,
+  // 32-bit buffer ranges per segment
+  const Split sp = split_segments(BH, N, C, 512, 1, 8, DV * 2);
+  pl->P = sp.P;
+  pl->L = sp.L;
+  if (BH <= 0 || N == 0) return true;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t off = 0;
   pl->seg_off = off;

@@ -1,6 +1,7 @@
 """Parity at the full workload sizes, in the launch configuration the bench
-times (bf16 output for bf16 workloads), on sampled rows the fp64 oracle
-computes one by one."""
+times (bf16 output for bf16 workloads): every row where the fp64 oracle can
+afford it (N <= 8192), else every row around each chunk and segment boundary
+plus a seeded random set; per head and per row (tests/helpers.py)."""
 import math
 import sys
 
@@ -9,7 +10,7 @@ import pytest
 
 from oracle import taylor_oracle as T
 import workloads as W
-from tests.helpers import normwise_rel, sample_rows, to_device, to_f64
+from tests.helpers import TOL, boundary_rows, check_parity, normwise_rel, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +20,6 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import taylor_series_linear_amd as tl  # noqa: E402
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def say(*a):
@@ -40,12 +40,17 @@ def test_prefill_workload(name):
     torch.cuda.synchronize()
     say("  kernel done")
     o = to_f64(o)
-    rows = sample_rows(w.N) if w.N > 512 else np.arange(w.N)
-    ref = T.direct(x["q64"], x["k64"], x["v64"], w.n_terms, w.a, rows=rows)
-    err = normwise_rel(o[:, :, rows], ref)
-    say("  normwise rel err (sampled rows)", err)
-    assert err < TOL[w.dtype]
     assert np.all(np.isfinite(o))
+    if w.N <= 8192:
+        rows = np.arange(w.N)
+    else:
+        # both large-feature kernels use 32-token chunks and segments of a
+        # multiple of 32 tokens: the chunk before and after every 1024th
+        # token, two rows at every chunk edge, 1024 random rows
+        rows = np.union1d(boundary_rows(w.N, 1024, span=33), boundary_rows(w.N, 32, span=1, extra=1024, seed=5))
+    say(f"  oracle on {len(rows)} rows per head")
+    ref = T.direct(x["q64"], x["k64"], x["v64"], w.n_terms, w.a, rows=rows)
+    check_parity(o[:, :, rows], ref, w.dtype, say=say)
     # state of two heads against the oracle's
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     for b, h in heads:
@@ -88,8 +93,6 @@ def test_decode_workload():
         rows = [w.N + s for s in check_steps]
         ref = T.direct(qq, kk, vv, w.n_terms, w.a, rows=rows)
         got = np.stack([to_f64(outs[s][b, h]) for s in check_steps])
-        err = normwise_rel(got[None], ref[None], 1)
-        say("   head", (b, h), "err", err)
-        assert err < TOL["f32"]
+        check_parity(got[None], ref[None], "f32", 1, say=say, what=f"head {(b, h)}: ")
         Sr, zr = T.state(kk, vv, w.n_terms)
         assert normwise_rel(to_f64(S[b, h])[None], Sr[None], 1) < TOL["f32"]
