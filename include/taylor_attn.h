@@ -154,6 +154,29 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Allocation-free prefill, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, results and errors as taylor_attn_prefill,
+ * without the workspace: the call's scratch (per-segment state sums,
+ * final-state staging, ticket counters) lives in a static device array of
+ * TAYLOR_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends. The call allocates and frees nothing.
+ *  - Sizes whose workspace (taylor_attn_prefill_workspace) exceeds
+ *    TAYLOR_NOALLOC_SCRATCH_BYTES return TAYLOR_ERR_WORKSPACE.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents: calls that overlap on one GPU (other streams, other
+ *    threads) race and give wrong results. Serialise them (one stream).
+ *  - The first call on a device looks the array's device address up (once
+ *    per device, with the stream's device current).
+ */
+#define TAYLOR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+taylor_status taylor_attn_prefill_noalloc(const void* q, const void* k, const void* v,
+                                          taylor_dtype in_dtype, int B, int H, int N, int d, int dv,
+                                          int n_terms, float a, const float* S0, const float* z0,
+                                          void* o, taylor_dtype out_dtype, float* S, float* z,
+                                          void* stream);
+
+/*
  * One generation step for B x H heads: update the state with (k, v), then
  * read out with q (update before read-out, as in S_t = S_{t-1} + v_t phi(k_t)^T,
  * o_t = S_t phi(q_t)).

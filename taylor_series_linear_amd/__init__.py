@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
     L.taylor_attn_prefill.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                       vp, vp, vp, i32, vp, vp, vp, sz, vp]
     L.taylor_attn_prefill.restype = i32
+    L.taylor_attn_prefill_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                              vp, vp, vp, i32, vp, vp, vp]
+    L.taylor_attn_prefill_noalloc.restype = i32
     L.taylor_attn_decode.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                      vp, vp, vp, i32, vp]
     L.taylor_attn_decode.restype = i32

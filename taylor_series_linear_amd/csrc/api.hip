@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "features.hpp"
@@ -178,13 +179,50 @@ taylor_status taylor_feature_map(const void* x, taylor_dtype x_dtype, int64_t ro
 
 namespace {
 
+// Scratch of the allocation-free prefill (taylor_attn_prefill_noalloc): its
+// per-segment state sums, final-state staging and ticket counters live here
+// instead of in a caller-provided workspace. Every GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` is a
+// host-side stand-in, not a device address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress with that device current, once
+// per device, and only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = TAYLOR_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of this GPU's scratch for work enqueued on `stream` (the
+// stream's device; the current device for the null stream).
+taylor_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  dev = cur;
+  if (stream != nullptr && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess)
+    return hip_status(e, "hipStreamGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(TAYLOR_ERR_HIP, "device index out of range for the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return TAYLOR_OK;
+}
+
 // Shared by the plain and the decayed prefill; `decay` selects the kernel
 // family (the decayed one also runs gamma = 1, so its workspace size does not
 // depend on gamma).
 taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B, int H,
                            int N, int d, int dv, int n_terms, float a, const taylor_attn_ext* ext, const float* S0,
                            const float* z0, void* o, taylor_dtype out_dtype, float* S, float* z,
-                           void* workspace, size_t ws_bytes, void* stream) {
+                           void* workspace, size_t ws_bytes, void* stream, bool use_scratch = false) {
   tl::PrefillPlan p;
   const bool extk = ext != nullptr;
   taylor_status s = check_prefill_shape(B, H, N, d, dv, n_terms, in_dtype, extk, &p);
@@ -199,10 +237,23 @@ taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_d
   const int BH = B * H;
   if (BH > 0 && N > 0 && (q == nullptr || k == nullptr || v == nullptr))
     return fail(TAYLOR_ERR_NULL_PTR, "q, k and v are required");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_scratch) {
+    if (p.bytes > kScratchBytes)
+      return fail(TAYLOR_ERR_WORKSPACE, "these sizes need " + std::to_string(p.bytes) +
+                                            " bytes of scratch, more than the " + std::to_string(kScratchBytes) +
+                                            " bytes of the allocation-free call; use taylor_attn_prefill with a "
+                                            "workspace");
+    if (BH == 0 || N == 0) {
+      workspace = nullptr;
+    } else if (p.bytes > 0) {
+      if ((s = scratch_address(st, &workspace)) != TAYLOR_OK) return s;
+    }
+    ws_bytes = kScratchBytes;
+  }
   if (p.bytes > 0 && (workspace == nullptr || ws_bytes < p.bytes))
     return fail(TAYLOR_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.bytes) +
                                           " bytes, got " + std::to_string(ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (BH == 0) return TAYLOR_OK;
   (void)hipGetLastError();  // report only errors of the launches below
   if (N == 0) {
@@ -303,6 +354,14 @@ taylor_status taylor_attn_prefill(const void* q, const void* k, const void* v,
                                   void* workspace, size_t ws_bytes, void* stream) {
   return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, nullptr, S0, z0, o, out_dtype, S, z,
                       workspace, ws_bytes, stream);
+}
+
+taylor_status taylor_attn_prefill_noalloc(const void* q, const void* k, const void* v, taylor_dtype in_dtype, int B,
+                                          int H, int N, int d, int dv, int n_terms, float a, const float* S0,
+                                          const float* z0, void* o, taylor_dtype out_dtype, float* S, float* z,
+                                          void* stream) {
+  return prefill_impl(q, k, v, in_dtype, B, H, N, d, dv, n_terms, a, nullptr, S0, z0, o, out_dtype, S, z, nullptr,
+                      0, stream, true);
 }
 
 size_t taylor_attn_prefill_decayed_workspace(int B, int H, int N, int d, int dv, int n_terms,

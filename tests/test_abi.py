@@ -21,7 +21,8 @@ def test_every_declared_function_is_exported():
                           "taylor_attn_prefill", "taylor_attn_decode",
                           "taylor_attn_prefill_decayed_workspace", "taylor_attn_prefill_decayed",
                           "taylor_attn_decode_decayed", "taylor_attn_prefill_ext_workspace",
-                          "taylor_attn_prefill_ext", "taylor_attn_decode_ext"}
+                          "taylor_attn_prefill_ext", "taylor_attn_decode_ext",
+                          "taylor_attn_prefill_noalloc"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -183,3 +184,18 @@ def test_ext_entry_points_reject_bad_arguments():
         assert dec(ext) == TAYLOR_ERR_BAD_SCALE, kw
     assert (L.taylor_attn_prefill_ext_workspace(2, 8, 8192, 16, 64, 5, TAYLOR_BF16)
             == L.taylor_attn_prefill_decayed_workspace(2, 8, 8192, 16, 64, 5, TAYLOR_BF16))
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    # the order-4 workload's workspace is larger than the static scratch;
+    # the size check comes before any device call
+    need = L.taylor_attn_prefill_workspace(2, 8, 8192, 16, 64, 5, TAYLOR_BF16)
+    assert need > (128 << 20)
+    st = L.taylor_attn_prefill_noalloc(FAKE, FAKE, FAKE, TAYLOR_BF16, 2, 8, 8192, 16, 64, 5, 4.0, None, None,
+                                       FAKE, TAYLOR_BF16, None, None, None)
+    assert st == TAYLOR_ERR_WORKSPACE
+    assert b"scratch" in L.taylor_last_error()
+    # argument errors are reported as by taylor_attn_prefill
+    st = L.taylor_attn_prefill_noalloc(FAKE, FAKE, FAKE, TAYLOR_BF16, 1, 2, 64, 16, 64, 2, 4.0, None, None,
+                                       FAKE, TAYLOR_BF16, None, None, None)
+    assert st == TAYLOR_ERR_UNSUPPORTED
