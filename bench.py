@@ -1,19 +1,23 @@
 """Benchmark: causal Taylor-series linear attention on one MI355X.
 
-One "step" is one taylor_attn_prefill call over the Based-style order-2
-workload (B=4, H=16, N=4096, d=16 -> 153 symmetric features, dv=64, bf16 in
-and out, fp32 accumulation, a = sqrt(d)): feature maps, score tiles,
-read-out, intra-chunk term, state update and normalisation all run inside
-that call. Inputs rotate over several resident replicas whose total exceeds
-the 256 MiB last-level cache, so every step reads them from HBM.
+One "step" is one taylor_attn_prefill call over the long-context order-2
+workload (B=1, H=8, N=65536, d=64 -> 2145 symmetric features, dv=64, bf16 in
+and out, fp32 accumulation, a = sqrt(d) = 8): feature maps, score tiles,
+read-out, intra-chunk term, state update, segment prefix and normalisation
+all run inside that call. It is the largest single-GPU configuration and the
+one whose cost is matrix-core bound ("Expanding Attention", "Time"), so the
+headline roofline is the bf16 MFMA peak. Inputs rotate over resident
+replicas whose total exceeds the 256 MiB last-level cache, so every step
+reads them from HBM.
 
-Printed: ONE JSON line with the prefill throughput (tokens/s) and its MFMA
-fraction, the decode state bandwidth of the order-2 decode workload (64 x 16
-heads, states seeded by a 32768-token prefill) as a fraction of HBM peak, the
-roofline of the dominant kernel and the fp64 CPU oracle timed beside it.
+Printed: ONE JSON line with the headline prefill (tokens/s, roofline against
+the bf16 MFMA peak, HBM traffic from counters), extra blocks for the
+Based-style order-2 prefill (HBM-bound), the order-4 prefill and the order-2
+decode (state bandwidth against HBM peak), and the fp64 CPU oracle timed
+beside it on all host cores and on one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--no-decode] [--no-native] [--only prefill|decode|copy]
+       [--no-decode] [--no-extra] [--no-native] [--only prefill|decode|copy]
 """
 from __future__ import annotations
 
@@ -32,25 +36,37 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 FP32_DENSE_TFLOPS = 157.3
-PREFILL = "based_order2_prefill"
+HEADLINE = "long_order2_prefill"
 DECODE = "order2_decode"
-CHUNK = 32                      # tokens per chunk of the order-2 d=16 bf16 kernel
-TRAFFIC = os.path.join(ROOT, "profiles", "traffic_based_order2_prefill.json")
+CHUNK = 32                      # tokens per chunk of every timed bf16 prefill kernel
+
+# Timed prefill workloads: the HIP sources their kernels are compiled from
+# (a stored counter record is used only while these are unchanged), the
+# roofline that binds them, and the input replicas that keep them out of the
+# last-level cache.
+PREFILLS = {
+    "long_order2_prefill": dict(sources=("prefill_w2.hip", "internal.hpp", "mma.hpp", "sched.hpp"),
+                                bound="mfma", replicas=2),
+    "based_order2_prefill": dict(sources=("prefill_o2.hip", "internal.hpp", "mma.hpp", "sched.hpp"),
+                                 bound="hbm", replicas=4),
+    "order4_prefill": dict(sources=("prefill.hip", "features.hpp", "internal.hpp", "mma.hpp", "sched.hpp"),
+                           bound="mfma", replicas=8),
+}
 
 
-# sources the timed order-2 d=16 bf16 prefill kernel is compiled from
-TIMED_SOURCES = ("prefill_o2.hip", "internal.hpp", "mma.hpp")
+def traffic_path(name):
+    return os.path.join(ROOT, "profiles", f"traffic_{name}.json")
 
 
-def source_hash():
-    """Hash of the timed kernel's HIP sources, to tell whether stored counter
+def source_hash(name=HEADLINE):
+    """Hash of a timed kernel's HIP sources, to tell whether stored counter
     data still describes the kernel being timed."""
     import hashlib
     csrc = os.path.join(ROOT, "taylor_series_linear_amd", "csrc")
     h = hashlib.sha256()
-    for name in TIMED_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    for fn in PREFILLS[name]["sources"]:
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -67,11 +83,13 @@ def _pmc_rows(d):
     return rows
 
 
-def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
-    """Turn four rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE of the prefill
-    bench; the same two counters over bench.py --only copy) into per-call HBM
-    bytes. The counters report KiB per dispatch; each is scaled by the ratio
-    of the plain copy's known bytes to what the same counter reads for it."""
+def pmc_summary(name, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE of one prefill
+    workload's calls; the same two counters over bench.py --only copy) into
+    per-call HBM bytes. The counters report KiB per dispatch; each is scaled
+    by the ratio of the plain copy's known bytes to what the same counter
+    reads for it. Every kernel of the library counts (all launches of one
+    call), the copy and torch's own kernels do not."""
     copy_bytes = 256 * 1024 * 1024
 
     def per_kernel(rows, counter):
@@ -91,26 +109,26 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, out_path):
     write = per_kernel(_pmc_rows(write_dir), "WRITE_SIZE")
     kernels = {}
     for k in sorted(set(fetch) | set(write)):
-        if "o2_" not in k and "prefill" not in k:
+        if "tl::" not in k:
             continue
         kernels[k] = {"fetch_bytes": fetch.get(k, 0.0) * f_scale, "write_bytes": write.get(k, 0.0) * w_scale}
     total = sum(v["fetch_bytes"] + v["write_bytes"] for v in kernels.values())
-    rec = {"workload": PREFILL, "source_hash": source_hash(), "fetch_scale": f_scale, "write_scale": w_scale,
+    rec = {"workload": name, "source_hash": source_hash(name), "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_kernel": ck, "kernels": kernels, "bytes_per_call": total}
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
 
-def stored_traffic():
+def stored_traffic(name=HEADLINE):
     """HBM bytes per prefill call from the stored counter summary, or None if
     the kernels changed since it was taken."""
     try:
-        with open(TRAFFIC) as f:
+        with open(traffic_path(name)) as f:
             rec = json.load(f)
     except OSError:
         return None
-    return rec["bytes_per_call"] if rec.get("source_hash") == source_hash() else None
+    return rec["bytes_per_call"] if rec.get("source_hash") == source_hash(name) else None
 
 
 def feature_dim(d, n_terms):
@@ -156,23 +174,29 @@ def time_loop(fn, steps, torch):
     return start.elapsed_time(end) / steps
 
 
-def bench_prefill(args, torch, tl, W):
-    w = W.WORKLOADS[PREFILL]
+def bench_prefill(name, steps, warmup, torch, tl, W, replicas=None):
+    """Time `steps` taylor_attn_prefill calls of a named workload (bf16 or
+    fp32 in, output in the input dtype), inputs rotating over resident
+    replicas. Returns the workload, ms per call, algorithmic bytes and flops
+    per call, the feature width, the replica count and the host inputs."""
+    w = W.WORKLOADS[name]
     x = W.make_workload(w)
-    reps = args.replicas
+    reps = replicas or PREFILLS[name]["replicas"]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = tl.TAYLOR_BF16 if w.dtype == "bf16" else tl.TAYLOR_F32
     qs = [dev_tensor(x["q"], w.dtype, torch) for _ in range(reps)]
     ks = [dev_tensor(x["k"], w.dtype, torch) for _ in range(reps)]
     vs = [dev_tensor(x["v"], w.dtype, torch) for _ in range(reps)]
-    os_ = [torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device="cuda") for _ in range(reps)]
-    ws_bytes = tl.prefill_workspace_bytes(w.B, w.H, w.N, w.d, w.dv, w.n_terms, torch.bfloat16)
+    os_ = [torch.empty((w.B, w.H, w.N, w.dv), dtype=tdt, device="cuda") for _ in range(reps)]
+    ws_bytes = tl.prefill_workspace_bytes(w.B, w.H, w.N, w.d, w.dv, w.n_terms, tdt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     L = tl.lib()
 
     # every call's arguments are built before the timed loop, so the loop only
-    # enqueues launches
+    # enqueues launches (on torch's current stream, which the events time)
     stream = tl._stream().value
-    calls = [(qs[r].data_ptr(), ks[r].data_ptr(), vs[r].data_ptr(), tl.TAYLOR_BF16, w.B, w.H, w.N, w.d, w.dv,
-              w.n_terms, w.a, None, None, os_[r].data_ptr(), tl.TAYLOR_BF16, None, None, ws.data_ptr(),
+    calls = [(qs[r].data_ptr(), ks[r].data_ptr(), vs[r].data_ptr(), code, w.B, w.H, w.N, w.d, w.dv,
+              w.n_terms, w.a, None, None, os_[r].data_ptr(), code, None, None, ws.data_ptr(),
               ws_bytes, stream) for r in range(reps)]
 
     def step(i):
@@ -180,11 +204,33 @@ def bench_prefill(args, torch, tl, W):
         if st != 0:
             tl.check(st)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
-    ms = time_loop(step, args.steps, torch)
+    ms = time_loop(step, steps, torch)
     bytes_, flops, F = algorithmic_prefill(w)
+    del qs, ks, vs, os_, ws
     return w, ms, bytes_, flops, F, reps, x
+
+
+def prefill_block(name, w, ms, bytes_, flops, F, reps, steps):
+    """Figures of one timed prefill workload: throughput, both roofs, counter
+    traffic (null unless the stored record matches the kernel's sources)."""
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = stored_traffic(name)
+    return {
+        "workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv, "n_terms": w.n_terms, "a": w.a,
+        "features": F, "dtype": w.dtype, "steps_timed": steps, "input_replicas": reps,
+        "ms_per_call": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+        "token_heads_per_s": w.B * w.H * w.N / (ms * 1e-3),
+        "mfma_tflops": tflops, "mfma_frac": tflops / BF16_DENSE_TFLOPS,
+        "hbm_GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+        "bound": PREFILLS[name]["bound"],
+        "traffic_bytes_per_call": traffic,
+        "traffic_over_algorithmic": None if traffic is None else traffic / bytes_,
+        "note": f"algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head with c={CHUNK}; "
+                "bytes (2d+dv)*in+dv*out per token-head",
+    }
 
 
 def bench_decode(args, torch, tl, W):
@@ -392,50 +438,96 @@ def time_workloads(names, torch, tl, W, reps=20):
         del q, k, v, o, ws
 
 
-def cpu_baseline(w, x, budget_s):
-    """fp64 oracle direct() on the first heads of the same inputs until ~budget_s."""
+def _van_der_corput_blocks(nb):
+    """Block indices 0..nb-1 in base-2 radical-inverse order: every prefix of
+    the list spreads over the whole sequence, so a sample cut short anywhere
+    covers early and late rows alike."""
+    order, seen = [], set()
+    bits = max(1, (nb - 1).bit_length())
+    for i in range(1 << bits):
+        r = int(format(i, f"0{bits}b")[::-1], 2)
+        if r < nb and r not in seen:
+            seen.add(r)
+            order.append(r)
+    return order
+
+
+def _oracle_leg(w, x, budget_s, block=256):
+    """fp64 oracle direct() over 256-row query blocks of the workload's own
+    inputs (blocks in radical-inverse order, heads in turn) until budget_s.
+    Row t costs t + 1 key columns, so the rate is converted to whole-workload
+    rows by work: equivalent token-heads = sum over sampled rows of (t + 1)
+    divided by the workload's mean (N + 1) / 2."""
     from oracle import taylor_oracle as T
+    nb = (w.N + block - 1) // block
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    work = 0
+    blocks = 0
+    t0 = time.perf_counter()
+    for i, blk in enumerate(_van_der_corput_blocks(nb) * len(heads)):
+        b, h = heads[i % len(heads)]
+        rows = np.arange(blk * block, min(w.N, (blk + 1) * block))
+        T.direct(x["q64"][b, h], x["k64"][b, h], x["v64"][b, h], w.n_terms, w.a, rows=rows)
+        work += int(np.sum(rows + 1))
+        blocks += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    token_heads = work / ((w.N + 1) / 2.0)
+    return token_heads / dt / w.H, dt, blocks
+
+
+def cpu_baseline(w, x, budget_s):
+    """The fp64 oracle on the host cores, over a bounded sample of the same
+    workload: all cores (BLAS threads as configured), then one thread, as the
+    pages' own implementation runs ("Expanding Attention", defaults
+    paragraph: single-threaded NumPy)."""
     try:
         import threadpoolctl
         threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
     except Exception:  # noqa: BLE001
+        threadpoolctl = None
         threads = os.cpu_count() or 1
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done = 0
-    t0 = time.perf_counter()
-    for (b, h) in heads:
-        T.direct(x["q64"][b, h], x["k64"][b, h], x["v64"][b, h], w.n_terms, w.a)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    token_heads = done * w.N
-    return {"value": token_heads / dt / w.H, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {len(heads)} heads, all {w.N} rows each, fp64 numpy direct(); "
-                      f"tokens/s = token-heads/s / H; {dt:.1f} s"}
+    sample = ("256-row query blocks of the same inputs in radical-inverse order over the sequence, heads in turn, "
+              "fp64 numpy direct(); rate converted to whole-workload rows by work (row t costs t+1 keys); "
+              "tokens/s = token-heads/s / H")
+    v, dt, nblk = _oracle_leg(w, x, budget_s)
+    out = {"value": v, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{sample}; {nblk} blocks in {dt:.1f} s"}
+    if threadpoolctl is not None:
+        with threadpoolctl.threadpool_limits(1):
+            v1, dt1, nb1 = _oracle_leg(w, x, budget_s)
+        out["single_thread"] = {"value": v1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                "sample": f"same recipe on one BLAS thread; {nb1} blocks in {dt1:.1f} s"}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--replicas", type=int, default=None)
     ap.add_argument("--decode-replicas", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the order-2 d=16 and order-4 prefill blocks")
     ap.add_argument("--no-native", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(PREFILLS),
+                    help="prefill workload of --only prefill")
     ap.add_argument("--time", nargs="+", metavar="WORKLOAD",
                     help="time one prefill call of each named workload, then exit")
     ap.add_argument("--sweep", action="store_true",
                     help="growth of prefill time with N and of decode time with the context, then exit")
-    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="summarise rocprofv3 --pmc runs into the stored traffic record and exit")
+    ap.add_argument("--pmc-summary", nargs=5,
+                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="summarise rocprofv3 --pmc runs into the workload's stored traffic record and exit")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary, TRAFFIC)
+        name = args.pmc_summary[0]
+        pmc_summary(name, *args.pmc_summary[1:], traffic_path(name))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -467,14 +559,19 @@ def main():
     if args.only == "decode":
         print(json.dumps(bench_decode(args, torch, tl, W)))
         return
+    if args.only == "prefill":
+        r = bench_prefill(args.workload, args.steps, args.warmup, torch, tl, W, args.replicas)
+        print(json.dumps(prefill_block(args.workload, *r[:6], args.steps)))
+        return
 
-    w, ms, bytes_, flops, F, reps, x = bench_prefill(args, torch, tl, W)
-    tokens = w.B * w.N
-    gbs = bytes_ / (ms * 1e-3) / 1e9
+    log(f"prefill: {HEADLINE}, {args.steps} timed calls")
+    w, ms, bytes_, flops, F, reps, x = bench_prefill(HEADLINE, args.steps, args.warmup, torch, tl, W,
+                                                     args.replicas)
     tflops = flops / (ms * 1e-3) / 1e12
+    gbs = bytes_ / (ms * 1e-3) / 1e9
     out = {
         "metric": "prefill tokens/s + MFMA % peak; decode state GB/s % HBM peak (1 GPU)",
-        "value": tokens / (ms * 1e-3),
+        "value": w.B * w.N / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -485,23 +582,33 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": PREFILL, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
+        "config": {"workload": HEADLINE, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dv": w.dv,
                    "n_terms": w.n_terms, "a": w.a, "features": F, "in": "bf16", "out": "bf16",
                    "accumulate": "fp32", "input_replicas": reps, "seed": w.seed},
         "token_heads_per_s": w.B * w.H * w.N / (ms * 1e-3),
-        "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_DENSE_TFLOPS,
-                 "frac": tflops / BF16_DENSE_TFLOPS, "flops_per_step": flops,
-                 "note": "algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head, c=32"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": stored_traffic(),
-                     "kernel": "one taylor_attn_prefill call: flag reset + single-pass o2 kernel (2 launches)",
-                     "launch_us": ms * 1e3, "algorithmic_bytes_per_launch": bytes_},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_DENSE_TFLOPS, "traffic": stored_traffic(HEADLINE),
+                     "kernel": "one taylor_attn_prefill call (all its launches), timed by HIP events on the "
+                               "stream the library launches on",
+                     "launch_us": ms * 1e3, "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": bytes_,
+                     "note": f"algorithmic flops 4F(dv+1)+(c+1)(d+dv+1) per token-head, c={CHUNK}; traffic = "
+                             "HBM bytes per call from FETCH_SIZE/WRITE_SIZE scaled by a plain copy"},
+        "hbm": {"achieved_GBps": gbs, "frac": gbs / HBM_PEAK_GBS},
     }
-    if args.only != "prefill" and not args.no_decode:
+    if not args.no_extra:
+        for name in ("based_order2_prefill", "order4_prefill"):
+            log(f"prefill: {name}")
+            st = max(args.steps, 50) if name == "based_order2_prefill" else args.steps
+            r = bench_prefill(name, st, args.warmup, torch, tl, W)
+            out[name] = prefill_block(name, *r[:6], st)
+            del r
+    if not args.no_decode:
         out["decode"] = bench_decode(args, torch, tl, W)
-    if not args.no_native and args.only is None:
+    if not args.no_native:
         out["native_c_abi"] = native_c_abi()
-    if not args.no_cpu and args.only is None:
+    if not args.no_cpu:
+        log("cpu oracle: all cores, then one thread")
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(out))
 

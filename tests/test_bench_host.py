@@ -8,6 +8,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import bench
@@ -34,6 +35,26 @@ def test_algorithmic_counts_of_the_bench_workload():
     assert bench.algorithmic_prefill(w, chunk=1024)[1] == th * (4 * 153 * 65 + 257 * 81)
 
 
+def test_algorithmic_counts_of_the_headline_workload():
+    # the long-context order-2 workload: d = 64 gives F = 2145 features
+    w = W.WORKLOADS[bench.HEADLINE]
+    assert (w.B, w.H, w.N, w.d, w.dv, w.n_terms, w.dtype, w.a) == (1, 8, 65536, 64, 64, 3, "bf16", 8.0)
+    bytes_, flops, F = bench.algorithmic_prefill(w, chunk=32)
+    assert F == 2145 == math.comb(66, 2)
+    th = 8 * 65536
+    assert bytes_ == th * (2 * 64 + 64) * 2 + th * 64 * 2
+    assert flops == th * (4 * 2145 * 65 + 33 * 129)
+
+
+def test_oracle_sample_blocks_cover_the_sequence():
+    # every block once, and the first blocks spread over the whole sequence
+    order = bench._van_der_corput_blocks(256)
+    assert sorted(order) == list(range(256))
+    assert order[:4] == [0, 128, 64, 192]
+    first = np.array(order[:16])
+    assert abs(first.mean() - 127.5) < 16
+
+
 def _write_pmc(dirname, counter, values):
     os.makedirs(dirname, exist_ok=True)
     with open(os.path.join(dirname, "p_counter_collection.csv"), "w", newline="") as f:
@@ -58,8 +79,8 @@ def test_pmc_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     _write_pmc(tmp_path / "pf", "FETCH_SIZE", {o2: [50000.0, 52000.0], reset: [1.0]})
     _write_pmc(tmp_path / "pw", "WRITE_SIZE", {o2: [52500.0], reset: [2.0]})
     out = tmp_path / "traffic.json"
-    bench.pmc_summary(str(tmp_path / "pf"), str(tmp_path / "pw"), str(tmp_path / "cf"), str(tmp_path / "cw"),
-                      str(out))
+    bench.pmc_summary("based_order2_prefill", str(tmp_path / "pf"), str(tmp_path / "pw"), str(tmp_path / "cf"),
+                      str(tmp_path / "cw"), str(out))
     rec = json.loads(out.read_text())
     assert rec["fetch_scale"] == pytest.approx(2.0) and rec["write_scale"] == pytest.approx(1.0)
     assert rec["kernels"][o2]["fetch_bytes"] == pytest.approx(51000.0 * 1024 * 2)
@@ -67,11 +88,11 @@ def test_pmc_summary_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     total = (51000.0 * 2 + 52500.0 + 1.0 * 2 + 2.0) * 1024
     assert rec["bytes_per_call"] == pytest.approx(total)
     # the record is used only while the timed kernel's sources are unchanged
-    monkeypatch.setattr(bench, "TRAFFIC", str(out))
-    assert bench.stored_traffic() == pytest.approx(total)
+    monkeypatch.setattr(bench, "traffic_path", lambda name: str(out))
+    assert bench.stored_traffic("based_order2_prefill") == pytest.approx(total)
     rec["source_hash"] = "0" * 16
     out.write_text(json.dumps(rec))
-    assert bench.stored_traffic() is None
+    assert bench.stored_traffic("based_order2_prefill") is None
 
 
 def test_more_than_one_gpu_is_refused():
