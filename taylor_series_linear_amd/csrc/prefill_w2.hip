@@ -29,16 +29,22 @@
 // blocks, off-diagonal tiles counted twice.
 //
 // Work decomposition: one workgroup of 8 waves per (head, value half of 32
-// columns, segment). The 74 tiles (68 state, 6 Gram) are split over the
-// waves, 9 or 10 each, as fp32 accumulators. Per 32-token chunk every wave
-// reads out its state tiles into a partial output, updates them, and (for
-// Gram tiles) updates Z and adds its part of the denominator; wave 0 also
-// computes the diagonal block (scores, weights, causal mask, P V). Partial
-// outputs meet in double-buffered LDS and all threads normalise and store
-// the previous chunk. Feature fragments are built with packed fp16
-// products: keys from an fp16 K'^T, queries from an fp16 q/a row that
-// carries duplicated, one and zero regions so every fragment is two
-// contiguous reads.
+// columns, segment). The 71 slots (68 state tiles, 3 Gram tiles) are spread
+// over the waves as fp32 accumulators: waves 0..6 hold 9 or 10 pair-class
+// tiles each, grouped so that one wave's tiles share their first coordinate
+// range (at most two such groups per wave); wave 7 holds the linear,
+// constant and Gram tiles, the key sum z1 and the diagonal block (scores,
+// weights, causal mask, P V). Per 32-token chunk every wave reads its tiles
+// out into a partial output, then updates them. Partial outputs meet in
+// double-buffered LDS and all threads normalise and store the previous chunk.
+//
+// Feature fragments. Key side (update, fp16 MFMA): packed fp16 products of
+// two rows of an fp16 K'^T tile. Query side (read-out, bf16 MFMA against the
+// state rounded to bf16): each lane holds, per 16-deep k-step, the q/a values
+// its tiles need in fp32 registers (one contiguous block per group, loaded
+// once per chunk from an fp32 q/a row that repeats its 64 coordinates), and
+// forms every feature with one fp32 multiply; pairs are rounded to bf16 with
+// one conversion. No LDS read per tile on the query side.
 //
 // Segments (states are additive, closing paragraph of the same page): a
 // first launch sums segments 0..P-2, a scan makes inclusive prefixes, the
@@ -64,21 +70,8 @@ constexpr int C = 32;                     // tokens per chunk
 constexpr int NW = 8, NTHR = NW * 64;
 constexpr int F = 2145;
 constexpr int NS = 68, NZ = 3, NSLOT = NS + NZ;
-constexpr int W_Z1 = 0;                   // wave that keeps z1 = sum of keys
-constexpr int W_DIAG = NW - 1;            // wave that computes the diagonal block
+constexpr int W_AUX = NW - 1;             // linear, constant and Gram slots, z1, diagonal block
 constexpr float kSqrt2 = 1.41421356237309515f;
-
-// slots [slot_begin(w), slot_begin(w+1)) belong to wave w. The diagonal
-// block costs its wave about three slots' time, so that wave holds 6 slots
-// and two others hold 10 (measured: with 9 slots everywhere but 8 on it,
-// the diagonal wave reached the chunk barrier last every time, 1.75 us
-// after the first of 8 us).
-__host__ __device__ constexpr int slot_begin(int w) {
-  constexpr int t[NW + 1] = {0, 9, 18, 28, 38, 47, 56, 65, NSLOT};
-  return w < NW ? t[w] : NSLOT;
-}
-static_assert(slot_begin(W_DIAG + 1) - slot_begin(W_DIAG) == 6, "the diagonal wave holds six slots");
-static_assert(slot_begin(NW) == NSLOT, "all slots assigned");
 
 enum { S_CLASS = 0, S_LIN = 1, S_CONST = 2, S_Z = 3 };
 struct Slot {
@@ -96,19 +89,130 @@ __host__ __device__ constexpr Slot slot_info(int s) {
   return Slot{S_Z, 0, 0, i == 2 ? 1 : 0, i == 0 ? 0 : 1};
 }
 
-// a range shared by every state slot of wave w (all of them pair classes),
-// or -1
-__host__ __device__ constexpr int uniform_abase(int w) {
-  int ab = -1;
-  for (int s = slot_begin(w); s < slot_begin(w + 1); ++s) {
-    const Slot t = slot_info(s);
-    if (t.kind == S_Z) continue;
-    if (t.kind != S_CLASS) return -1;
-    if (ab >= 0 && t.abase != ab) return -1;
-    ab = t.abase;
+// Slots of each wave. Pair classes of one first-coordinate range (abase)
+// and consecutive offsets K stay together, so a wave's query features come
+// from at most two register blocks. Wave 7 (linear, constant and Gram
+// tiles, z1, diagonal block) also takes two pair classes: per chunk it then
+// issues about as many VALU instructions as a wave of nine classes.
+constexpr int MAXSL = 10;
+struct SlotList {
+  int n;
+  int s[MAXSL];
+};
+__host__ __device__ constexpr SlotList wave_slots(int w) {
+  switch (w) {
+    case 0: return SlotList{9, {0, 1, 2, 3, 4, 5, 6, 7, 8}};
+    case 1: return SlotList{9, {9, 10, 11, 12, 13, 14, 15, 16, 17}};
+    case 2: return SlotList{9, {18, 19, 20, 21, 22, 23, 24, 25, 26}};
+    case 3: return SlotList{9, {27, 28, 29, 30, 31, 64, 32, 33, 34}};
+    case 4: return SlotList{9, {35, 36, 37, 38, 39, 40, 41, 42, 43}};
+    case 5: return SlotList{9, {44, 45, 46, 47, 48, 49, 50, 51, 52}};
+    case 6: return SlotList{9, {53, 54, 55, 56, 57, 58, 59, 60, 61}};
+    default: return SlotList{8, {62, 63, 65, 66, 67, 68, 69, 70}};
   }
-  return ab;
 }
+constexpr bool slots_partitioned() {
+  int hits[NSLOT] = {};
+  for (int w = 0; w < NW; ++w) {
+    const SlotList L = wave_slots(w);
+    for (int i = 0; i < L.n; ++i) {
+      if (L.s[i] < 0 || L.s[i] >= NSLOT) return false;
+      ++hits[L.s[i]];
+    }
+  }
+  for (int s = 0; s < NSLOT; ++s)
+    if (hits[s] != 1) return false;
+  for (int w = 0; w < W_AUX; ++w) {
+    const SlotList L = wave_slots(w);
+    for (int i = 0; i < L.n; ++i)
+      if (slot_info(L.s[i]).kind != S_CLASS) return false;
+  }
+  // the auxiliary wave's pair classes share the range of its second linear
+  // tile (abase 32), so its two key rows serve both
+  for (int i = 0; i < wave_slots(W_AUX).n; ++i) {
+    const Slot t = slot_info(wave_slots(W_AUX).s[i]);
+    if (t.kind == S_CLASS && t.abase != 32) return false;
+  }
+  return true;
+}
+static_assert(slots_partitioned(), "every slot on exactly one wave; waves 0..6 hold pair classes only");
+
+// Query-side register blocks of a wave: one per first-coordinate range of
+// its pair classes. A block holds, for one k-step, q/a at coordinates
+// abase + 16 ks + 4 lh + kb + [0, nb) (kb = smallest offset K rounded down to
+// a multiple of 4; nb covers the largest K plus the 12-wide span of a
+// lane's eight features).
+struct Group {
+  int abase, kb, nb;
+};
+__host__ __device__ constexpr int n_groups(int w) {
+  const SlotList L = wave_slots(w);
+  int ab0 = -1, n = 0;
+  for (int i = 0; i < L.n; ++i) {
+    const Slot t = slot_info(L.s[i]);
+    if (t.kind != S_CLASS) continue;
+    if (n == 0) {
+      ab0 = t.abase;
+      n = 1;
+    } else if (t.abase != ab0) {
+      n = 2;
+    }
+  }
+  return n;
+}
+__host__ __device__ constexpr int group_abase(int w, int g) {
+  const SlotList L = wave_slots(w);
+  int seen = -1, k = -1;
+  for (int i = 0; i < L.n; ++i) {
+    const Slot t = slot_info(L.s[i]);
+    if (t.kind != S_CLASS || t.abase == seen) continue;
+    seen = t.abase;
+    if (++k == g) return t.abase;
+  }
+  return -1;
+}
+__host__ __device__ constexpr Group group_of(int w, int g) {
+  const SlotList L = wave_slots(w);
+  const int ab = group_abase(w, g);
+  int kmin = 1 << 20, kmax = -1;
+  for (int i = 0; i < L.n; ++i) {
+    const Slot t = slot_info(L.s[i]);
+    if (t.kind != S_CLASS || t.abase != ab) continue;
+    kmin = t.koff < kmin ? t.koff : kmin;
+    kmax = t.koff > kmax ? t.koff : kmax;
+  }
+  const int kb = kmin & ~3;
+  return Group{ab, kb, ((kmax + 12 - kb) + 3) & ~3};
+}
+// Block of the pair classes of wave w with first-coordinate range ab (nb = 0
+// when the wave has none).
+__host__ __device__ constexpr Group group_for(int w, int ab) {
+  return group_abase(w, 0) == ab ? group_of(w, 0) : (group_abase(w, 1) == ab ? group_of(w, 1) : Group{ab, 0, 0});
+}
+// The two key-row / first-coordinate ranges a wave works with: its class
+// groups, or for the auxiliary wave the ranges of its linear and Gram tiles.
+__host__ __device__ constexpr int row_base(int w, int g) {
+  if (w == W_AUX) return 32 * g;
+  return g < n_groups(w) ? group_abase(w, g) : -1;
+}
+constexpr bool groups_fit() {
+  for (int w = 0; w < NW; ++w) {
+    if (n_groups(w) < 1 || n_groups(w) > 2) return false;
+    for (int g = 0; g < 2; ++g) {
+      const Group G = group_for(w, row_base(w, g));
+      // the block stays inside the repeated 128-float q/a row
+      if (G.abase + 16 + 4 + G.kb + G.nb > 128 || G.nb > 24) return false;
+    }
+    // every class tile of the wave belongs to one of its two ranges
+    const SlotList L = wave_slots(w);
+    for (int i = 0; i < L.n; ++i) {
+      const Slot t = slot_info(L.s[i]);
+      if (t.kind == S_CLASS && t.abase != row_base(w, 0) && t.abase != row_base(w, 1)) return false;
+    }
+  }
+  return true;
+}
+static_assert(groups_fit(), "query register blocks fit the repeated q/a row");
 
 // Canonical index and weight of state row r of state slot s.
 struct Feat {
@@ -144,17 +248,14 @@ static_assert(basis_is_bijective(), "internal basis covers the canonical one onc
 // LDS layout of one chunk buffer (bytes). Row pitches keep 16-byte alignment
 // and put consecutive rows on different banks.
 constexpr int QRP = 104;   // raw q (bf16): q[0..63], 1, zeros (Gram block 2)
-constexpr int QFP = 164;   // q/a (fp16): q/a[0..63], q/a[0..31], ones x32, zeros x32;
-                           // 82-dword rows: 8-byte reads of 32 rows hit 64 banks
+constexpr int QAP = 132;   // q/a (fp32): q/a[0..63], q/a[0..63] again; 4 pad
 constexpr int KRP = 72;    // raw k rows (bf16)
-constexpr int KTP = 40;    // K'^T rows (fp16): 0..63 coordinates, 64..95 = 0..31, 96 valid, 97 zero
+constexpr int KTP = 40;    // K'^T rows (fp16): coordinates 0..63, then 0..31 again
 constexpr int VTP = 40;    // V^T rows (fp16), this workgroup's 32 columns
-constexpr int KT_ROWS = 98;
-constexpr int ROW_VALID = 96, ROW_ZERO = 97;
-constexpr int QF_ONES = 96, QF_ONE_THEN_ZEROS = 127;
+constexpr int KT_ROWS = 96;
 constexpr int OFF_QR = 0;
-constexpr int OFF_QF = OFF_QR + C * QRP * 2;
-constexpr int OFF_KR = OFF_QF + C * QFP * 2;
+constexpr int OFF_QA = OFF_QR + C * QRP * 2;
+constexpr int OFF_KR = OFF_QA + C * QAP * 4;
 constexpr int OFF_KT = OFF_KR + C * KRP * 2;
 constexpr int OFF_VT = OFF_KT + KT_ROWS * KTP * 2;
 constexpr int BUF = OFF_VT + DH * VTP * 2;
@@ -167,7 +268,7 @@ constexpr int OFF_PDEN = OFF_PART + 2 * PART;
 constexpr int OFF_Z1 = OFF_PDEN + 2 * NW * C * 4;  // z1 as bf16, 64 entries
 constexpr int LDS = OFF_Z1 + 64 * 2;
 static_assert(LDS <= 160 * 1024, "one workgroup per CU");
-static_assert(OFF_QF % 16 == 0 && OFF_KR % 16 == 0 && OFF_KT % 16 == 0 && OFF_VT % 16 == 0 && BUF % 16 == 0 &&
+static_assert(OFF_QA % 16 == 0 && OFF_KR % 16 == 0 && OFF_KT % 16 == 0 && OFF_VT % 16 == 0 && BUF % 16 == 0 &&
                   OFF_PART % 16 == 0 && OFF_PDEN % 16 == 0,
               "16-byte aligned regions");
 
@@ -196,17 +297,8 @@ __device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
 __device__ __forceinline__ bf16x8 catb(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
-__device__ __forceinline__ bf16x8 h2b(f16x8 x) {
-  bf16x8 r;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) r[u] = static_cast<__bf16>(static_cast<float>(x[u]));
-  return r;
-}
-__device__ __forceinline__ f16x8 b2h(bf16x8 x, float scale) {
-  f16x8 r;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) r[u] = static_cast<_Float16>(static_cast<float>(x[u]) * scale);
-  return r;
+__device__ __forceinline__ f16x8 b2h(bf16x8 x) {
+  return __builtin_convertvector(__builtin_convertvector(x, f32x8), f16x8);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
@@ -214,7 +306,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
 }
-
 
 template <int B, class Fn, int... Is>
 __device__ __forceinline__ void static_for_impl(Fn&& fn, std::integer_sequence<int, Is...>) {
@@ -224,6 +315,10 @@ template <int B, int E, class Fn>
 __device__ __forceinline__ void static_for(Fn&& fn) {
   if constexpr (E > B) static_for_impl<B>(fn, std::make_integer_sequence<int, E - B>{});
 }
+
+// position, within a lane's eight features of a k-step, of element s: the
+// accumulator rows 16 ks + 4 lh + {0..3} and 16 ks + 8 + 4 lh + {0..3}
+__device__ __forceinline__ constexpr int fpos(int s) { return s < 4 ? s : s + 4; }
 
 enum { SEGSUM = 0, MAIN = 1 };
 
@@ -251,7 +346,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
 
   auto qr = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<__bf16*>(smem + b * BUF + OFF_QR); };
-  auto qf = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_QF); };
+  auto qa = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<float*>(smem + b * BUF + OFF_QA); };
   auto kr = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<__bf16*>(smem + b * BUF + OFF_KR); };
   auto kt = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_KT); };
   auto vt = [&](int b) __attribute__((always_inline)) { return reinterpret_cast<_Float16*>(smem + b * BUF + OFF_VT); };
@@ -260,14 +355,10 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     return reinterpret_cast<float*>(smem + OFF_PDEN) + b * NW * C;
   };
 
-  // constant regions of both buffers
+  // constant region of both buffers: Q' columns 64..95 = (1, 0, ...)
   for (int i = tid; i < 2 * C; i += NTHR) {
-    const int b = i / C, row = i % C;
-    _Float16* f = qf(b) + row * QFP;
-    for (int c = 96; c < 160; ++c) f[c] = static_cast<_Float16>(c < 128 ? 1.f : 0.f);
-    __bf16* r = qr(b) + row * QRP;
+    __bf16* r = qr(i / C) + (i % C) * QRP;
     for (int c = 64; c < 96; ++c) r[c] = static_cast<__bf16>(c == 64 ? 1.f : 0.f);
-    kt(b)[ROW_ZERO * KTP + row] = static_cast<_Float16>(0.f);
   }
 
   // staging -----------------------------------------------------------------
@@ -283,7 +374,8 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   };
   // item of this thread: threads 0..255 a Q item, 256..511 a K item (row
   // it >> 3, coordinates 8 (it & 7) .. +8); threads 0..127 also a V item
-  // (row tid >> 2, this half's columns 8 (tid & 3) .. +8)
+  // (row tid >> 2, this half's columns 8 (tid & 3) .. +8). Rows past the
+  // segment's end load as zero (buffer range), so they add nothing.
   const bool is_q = __builtin_amdgcn_readfirstlane(tid) < 256;
   const int it = is_q ? tid : tid - 256;
   const int irow = it >> 3, ic8 = it & 7;
@@ -295,24 +387,25 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   auto load_v = [&](int c) __attribute__((always_inline)) -> uint4 {
     return bload16(rv, (crow(c, vrow) * DV + DH * hv + 8 * vc4) * 2);
   };
-  uint4 ra[1], rvv[1];  // one chunk ahead: the chunk's compute covers the load latency
-  auto stage = [&](int c, int b, auto slot) __attribute__((always_inline)) {
-    constexpr int SL = decltype(slot)::value;
-    static_assert(SL == 0, "one ring slot");
-    const bf16x8 x = __builtin_bit_cast(bf16x8, ra[SL]);
+  uint4 ra, rvv;  // one chunk ahead: the chunk's compute covers the load latency
+  auto stage = [&](int c, int b) __attribute__((always_inline)) {
+    const bf16x8 x = __builtin_bit_cast(bf16x8, ra);
     if (MODE == MAIN && is_q) {
       *reinterpret_cast<bf16x8*>(qr(b) + irow * QRP + 8 * ic8) = x;
-      const f16x8 h = b2h(x, inv_a);
-      const f16x4 h0{h[0], h[1], h[2], h[3]}, h1{h[4], h[5], h[6], h[7]};
-      *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + 8 * ic8) = h0;
-      *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + 8 * ic8 + 4) = h1;
-      if (ic8 < 4) {
-        *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + D + 8 * ic8) = h0;
-        *reinterpret_cast<f16x4*>(qf(b) + irow * QFP + D + 8 * ic8 + 4) = h1;
+      f32x4 lo, hi;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lo[u] = static_cast<float>(x[u]) * inv_a;
+        hi[u] = static_cast<float>(x[u + 4]) * inv_a;
       }
+      float* row = qa(b) + irow * QAP + 8 * ic8;
+      *reinterpret_cast<f32x4*>(row) = lo;
+      *reinterpret_cast<f32x4*>(row + 4) = hi;
+      *reinterpret_cast<f32x4*>(row + D) = lo;
+      *reinterpret_cast<f32x4*>(row + D + 4) = hi;
     } else if (!is_q) {
       if (MODE == MAIN) *reinterpret_cast<bf16x8*>(kr(b) + irow * KRP + 8 * ic8) = x;
-      const f16x8 h = b2h(x, 1.f);
+      const f16x8 h = b2h(x);
       _Float16* t = kt(b);
 #pragma unroll
       for (int u = 0; u < 8; ++u) t[(8 * ic8 + u) * KTP + irow] = h[u];
@@ -320,117 +413,156 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) t[(D + 8 * ic8 + u) * KTP + irow] = h[u];
       }
-      if (ic8 == 0) t[ROW_VALID * KTP + irow] = static_cast<_Float16>(c * C + irow < static_cast<int>(seg_rows) ? 1.f : 0.f);
     }
     if (has_v) {
-      const f16x8 h = b2h(__builtin_bit_cast(bf16x8, rvv[SL]), 1.f);
+      const f16x8 h = b2h(__builtin_bit_cast(bf16x8, rvv));
       _Float16* t = vt(b);
 #pragma unroll
       for (int u = 0; u < 8; ++u) t[(8 * vc4 + u) * VTP + vrow] = h[u];
     }
-    ra[SL] = load_a(c + 1);
-    if (has_v) rvv[SL] = load_v(c + 1);
+    ra = load_a(c + 1);
+    if (has_v) rvv = load_v(c + 1);
   };
 
   // per-chunk compute ---------------------------------------------------------
   const float c2 = 0.5f * inv_a * inv_a;
-  const f16x8 halfh = f16x8{0.5f, 0.5f, 0.5f, 0.5f, 0.5f, 0.5f, 0.5f, 0.5f};
-  // K'^T row of Gram block `blk` for lane lc
   const float c2z = 0.5f * inv_a * inv_a;  // Z~ = Z / (2 a^2) on the key-coordinate blocks
-  // One chunk for wave W (compile-time slot list).
+  // One chunk for wave W (compile-time slot list): read out every slot into
+  // a partial output (before its update), then update every slot.
   auto compute_w = [&](auto wtag, auto& acc, float& z1r, int i, int b, bool out) __attribute__((always_inline)) {
     constexpr int W = decltype(wtag)::value;
-    constexpr int SB = slot_begin(W), NSW = slot_begin(W + 1) - SB;
+    constexpr SlotList SL = wave_slots(W);
+    constexpr int NSW = SL.n;
     const _Float16* K = kt(b);
     const _Float16* V = vt(b);
-    const _Float16* QF = qf(b) + lc * QFP;
+    const float* QA = qa(b) + lc * QAP;
     const __bf16* QR = qr(b) + lc * QRP;
     f32x16 O = f32x16{};
     float dpart = 0.f;
-    // operands shared by the chunk: V^T fragments; and, when every state
-    // slot of the wave covers the same a range, the a-side rows of both
-    // feature fragments
-    constexpr int UAB = uniform_abase(W);
-    f16x8 bv[2], aq[2], kx[2];
+    // the wave's two first-coordinate ranges and their query blocks
+    constexpr int NG = W == W_AUX ? 2 : n_groups(W);
+    constexpr int AB0 = row_base(W, 0);
+    constexpr int AB1 = NG > 1 ? row_base(W, 1) : AB0;
+    constexpr Group G0 = group_for(W, AB0);
+    constexpr Group G1 = group_for(W, AB1);
+    constexpr int NB0 = G0.nb > 0 ? G0.nb : 4, NB1 = G1.nb > 0 ? G1.nb : 4;
+
+    if (out) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bv[ks] = lds<f16x8>(V + lc * VTP + 16 * ks + 8 * lh);
-      if constexpr (UAB >= 0) {
-        const int o = UAB + 16 * ks + 4 * lh;
-        aq[ks] = cat(lds<f16x4>(QF + o), lds<f16x4>(QF + o + 8));
-        kx[ks] = lds<f16x8>(K + (UAB + lc) * KTP + 16 * ks + 8 * lh);
-      }
-    }
-    static_for<0, NSW>([&](auto sli) {
-      constexpr int sl = decltype(sli)::value;
-      constexpr Slot t = slot_info(SB + sl);
-      if constexpr (t.kind != S_Z) {
-        if (out) {
-          // read-out: O^T[dv][query] += S^T phi~(Q)^T, features in the
-          // accumulator order (rows 16ks + 4lh + 0..3 and 16ks + 8 + 4lh + 0..3)
-          constexpr int acol = t.kind == S_CONST ? QF_ONE_THEN_ZEROS : t.abase;
-          constexpr int bcol = t.kind == S_CLASS ? t.abase + t.koff : QF_ONES;
+      for (int ks = 0; ks < 2; ++ks) {
+        // q/a of the lane's query at its eight features' first coordinates,
+        // per range, and each range's block of second coordinates
+        float av[NG][8];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const int o = 16 * ks + 4 * lh;
-            f16x8 qa;
-            if constexpr (UAB >= 0)
-              qa = aq[ks];
-            else
-              qa = cat(lds<f16x4>(QF + acol + o), lds<f16x4>(QF + acol + o + 8));
-            f16x8 ph = qa * cat(lds<f16x4>(QF + bcol + o), lds<f16x4>(QF + bcol + o + 8));
-            if constexpr (t.kind == S_CLASS && t.koff == 0) ph = ph * halfh;
+        for (int g = 0; g < NG; ++g) {
+          const float* base = QA + (g == 0 ? AB0 : AB1) + 16 * ks + 4 * lh;
+          const f32x4 x0 = lds<f32x4>(base), x1 = lds<f32x4>(base + 8);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            av[g][u] = x0[u];
+            av[g][u + 4] = x1[u];
+          }
+        }
+        float blk0[NB0], blk1[NB1];
+        if constexpr (G0.nb > 0) {
+#pragma unroll
+          for (int u = 0; u < NB0 / 4; ++u) {
+            const f32x4 x = lds<f32x4>(QA + AB0 + 16 * ks + 4 * lh + G0.kb + 4 * u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) blk0[4 * u + e] = x[e];
+          }
+        }
+        if constexpr (NG > 1 && G1.nb > 0) {
+#pragma unroll
+          for (int u = 0; u < NB1 / 4; ++u) {
+            const f32x4 x = lds<f32x4>(QA + AB1 + 16 * ks + 4 * lh + G1.kb + 4 * u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) blk1[4 * u + e] = x[e];
+          }
+        }
+        static_for<0, NSW>([&](auto sli) {
+          constexpr int sl = decltype(sli)::value;
+          constexpr Slot t = slot_info(SL.s[sl]);
+          if constexpr (t.kind != S_Z) {
+            // read-out: O^T[dv][query] += S^T phi~(Q)^T, features in the
+            // accumulator order
+            bf16x8 ph;
+            if constexpr (t.kind == S_CLASS) {
+              constexpr int g = t.abase == AB0 ? 0 : 1;
+              constexpr int kb = g == 0 ? G0.kb : G1.kb;
+#pragma unroll
+              for (int s = 0; s < 8; ++s) {
+                const float y = (g == 0 ? blk0 : blk1)[fpos(s) + t.koff - kb];
+                const float x = t.koff == 0 ? 0.5f * av[g][s] : av[g][s];
+                ph[s] = static_cast<__bf16>(x * y);
+              }
+            } else if constexpr (t.kind == S_LIN) {
+              constexpr int g = t.abase == AB0 ? 0 : 1;
+#pragma unroll
+              for (int s = 0; s < 8; ++s) ph[s] = static_cast<__bf16>(av[g][s]);
+            } else {  // the constant: feature 0 only
+#pragma unroll
+              for (int s = 0; s < 8; ++s) ph[s] = static_cast<__bf16>(ks == 0 && s == 0 && lh == 0 ? 1.f : 0.f);
+            }
             bf16x8 sa;
 #pragma unroll
             for (int s = 0; s < 8; ++s) sa[s] = static_cast<__bf16>(acc[sl][8 * ks + s]);
-            O = mfma32(sa, h2b(ph), O);
-          }
-        }
-        // update: S += phi(K)^T V
-        const int arow = t.kind == S_CONST ? (lc == 0 ? ROW_VALID : ROW_ZERO) : t.abase + lc;
-        const int brow = t.kind == S_CLASS ? t.abase + lc + t.koff : ROW_VALID;
+            O = mfma32(sa, ph, O);
+          } else if (ks == 0) {
+            // denominator part: sum_{i in zr, j in zc} q_i Z~_ij q_j (x2 off
+            // the diagonal), as U = Z~^T q_zr then q_zc . U
+            f32x16 U = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f16x8 x;
-          if constexpr (UAB >= 0)
-            x = kx[ks];
-          else
-            x = lds<f16x8>(K + arow * KTP + 16 * ks + 8 * lh);
-          acc[sl] = mfma32h(x * lds<f16x8>(K + brow * KTP + 16 * ks + 8 * lh), bv[ks], acc[sl]);
-        }
-      } else {
-        if (out) {
-          // denominator part: sum_{i in zr, j in zc} q_i Z~_ij q_j (x2 off
-          // the diagonal), as U = Z~^T q_zr then q_zc . U
-          f32x16 U = f32x16{};
+            for (int kz = 0; kz < 2; ++kz) {
+              bf16x8 za;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 za;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-              const int j = 8 * ks + s;
-              za[s] = static_cast<__bf16>(acc[sl][j] * c2z);
+              for (int s = 0; s < 8; ++s) za[s] = static_cast<__bf16>(acc[sl][8 * kz + s] * c2z);
+              const int o = 32 * t.zr + 16 * kz + 4 * lh;
+              U = mfma32(za, catb(lds<bf16x4>(QR + o), lds<bf16x4>(QR + o + 8)), U);
             }
-            const int o = 32 * t.zr + 16 * ks + 4 * lh;
-            U = mfma32(za, catb(lds<bf16x4>(QR + o), lds<bf16x4>(QR + o + 8)), U);
+            float bil = 0.f;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const bf16x4 qv = lds<bf16x4>(QR + 32 * t.zc + 8 * g + 4 * lh);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bil += U[4 * g + e] * static_cast<float>(qv[e]);
+            }
+            dpart += (t.zr == t.zc ? 1.f : 2.f) * bil;
           }
-          float bil = 0.f;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const bf16x4 qv = lds<bf16x4>(QR + 32 * t.zc + 8 * g + 4 * lh);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bil += U[4 * g + e] * static_cast<float>(qv[e]);
-          }
-          dpart += (t.zr == t.zc ? 1.f : 2.f) * bil;
-        }
-        const int ar = 32 * t.zr + lc, br = 32 * t.zc + lc;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          acc[sl] = mfma32h(lds<f16x8>(K + ar * KTP + 16 * ks + 8 * lh), lds<f16x8>(K + br * KTP + 16 * ks + 8 * lh),
-                            acc[sl]);
+        });
       }
-    });
-    if constexpr (W == W_Z1) {
+    }
+    // update: S += phi(K)^T V (key products in fp16; rows past the segment's
+    // end are zero in K and V, so they add nothing). Operands shared by the
+    // wave's tiles: the V^T fragments and the key rows of its two ranges
+    // (every tile of a range multiplies by the same row of K'^T).
+    f16x8 bv[2], kx[NG][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bv[ks] = lds<f16x8>(V + lc * VTP + 16 * ks + 8 * lh);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) kx[g][ks] = lds<f16x8>(K + ((g == 0 ? AB0 : AB1) + lc) * KTP + 16 * ks + 8 * lh);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      static_for<0, NSW>([&](auto sli) {
+        constexpr int sl = decltype(sli)::value;
+        constexpr Slot t = slot_info(SL.s[sl]);
+        if constexpr (t.kind == S_CLASS) {
+          constexpr int g = t.abase == AB0 ? 0 : 1;
+          acc[sl] = mfma32h(kx[g][ks] * lds<f16x8>(K + (t.abase + t.koff + lc) * KTP + 16 * ks + 8 * lh), bv[ks],
+                            acc[sl]);
+        } else if constexpr (t.kind == S_LIN) {
+          acc[sl] = mfma32h(kx[t.abase == AB0 ? 0 : 1][ks], bv[ks], acc[sl]);
+        } else if constexpr (t.kind == S_CONST) {
+          const _Float16 one = static_cast<_Float16>(lc == 0 ? 1.f : 0.f);
+          acc[sl] = mfma32h(f16x8{one, one, one, one, one, one, one, one}, bv[ks], acc[sl]);
+        } else {
+          acc[sl] = mfma32h(kx[t.zr][ks], kx[t.zc][ks], acc[sl]);
+        }
+      });
+    }
+    if constexpr (W == W_AUX) {
       // linear part of the denominator, (q . z1) / a with z1 of the earlier
       // chunks (every row of the product equals q . z1), then z1 += keys
       if (out) {
@@ -442,42 +574,44 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
           U = mfma32(lds<bf16x8>(zb + 16 * ks + 8 * lh), lds<bf16x8>(QR + 16 * ks + 8 * lh), U);
         if (lh == 0) dpart += inv_a * U[0];
       }
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
       const _Float16* kr0 = K + l * KTP;
       float zs = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const f16x8 x = lds<f16x8>(kr0 + 8 * u);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zs += static_cast<float>(x[e]);
+        for (int e = 0; e < 4; ++e) zs = __builtin_amdgcn_fdot2(f16x2{x[2 * e], x[2 * e + 1]}, ones, zs, false);
       }
       z1r += zs;
+      if (out) {
+        // diagonal block: scores D[key][query] = K Q^T (raw), weights,
+        // causal mask, then O^T += V^T P^T with keys in the accumulator order
+        const __bf16* KR = kr(b) + lc * KRP;
+        f32x16 sc = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          sc = mfma32(lds<bf16x8>(KR + 16 * ks + 8 * lh), lds<bf16x8>(QR + 16 * ks + 8 * lh), sc);
+        f16x8 P0, P1;
+        float den = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float wv = __builtin_fmaf(__builtin_fmaf(c2, sc[j], inv_a), sc[j], 1.f);
+          if (acc_row(j, lh) > lc) wv = 0.f;
+          den += wv;
+          if (j < 8)
+            P0[j] = static_cast<_Float16>(wv);
+          else
+            P1[j - 8] = static_cast<_Float16>(wv);
+        }
+        const _Float16* vr = V + lc * VTP;
+        O = mfma32h(cat(lds<f16x4>(vr + 4 * lh), lds<f16x4>(vr + 8 + 4 * lh)), P0, O);
+        O = mfma32h(cat(lds<f16x4>(vr + 16 + 4 * lh), lds<f16x4>(vr + 24 + 4 * lh)), P1, O);
+        dpart += den;
+      }
     }
     if (!out) return;
-    if constexpr (W == W_DIAG) {
-      // diagonal block: scores D[key][query] = K Q^T (raw), weights, causal
-      // mask, then O^T += V^T P^T with keys in the accumulator order
-      const __bf16* KR = kr(b) + lc * KRP;
-      f32x16 sc = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sc = mfma32(lds<bf16x8>(KR + 16 * ks + 8 * lh), lds<bf16x8>(QR + 16 * ks + 8 * lh), sc);
-      f16x8 P0, P1;
-      float den = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float wv = __builtin_fmaf(__builtin_fmaf(c2, sc[j], inv_a), sc[j], 1.f);
-        if (acc_row(j, lh) > lc) wv = 0.f;
-        den += wv;
-        if (j < 8)
-          P0[j] = static_cast<_Float16>(wv);
-        else
-          P1[j - 8] = static_cast<_Float16>(wv);
-      }
-      const _Float16* vr = V + lc * VTP;
-      O = mfma32h(cat(lds<f16x4>(vr + 4 * lh), lds<f16x4>(vr + 8 + 4 * lh)), P0, O);
-      O = mfma32h(cat(lds<f16x4>(vr + 16 + 4 * lh), lds<f16x4>(vr + 24 + 4 * lh)), P1, O);
-      dpart += den;
-    }
     dpart += __shfl_xor(dpart, 32);
     // partial outputs: [wave][query lc][dv rows 8g + 4lh + 0..3]
     float* pt = part(i & 1) + (W * C + lc) * PP;
@@ -523,15 +657,14 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   };
 
   // everything that depends on the wave's slot list, per wave ---------------
-  using S0_ = std::integral_constant<int, 0>;
-  using S1_ = std::integral_constant<int, 1>;
   auto wave_body = [&](auto wtag) __attribute__((always_inline)) {
     constexpr int W = decltype(wtag)::value;
-    constexpr int SB = slot_begin(W), NSW = slot_begin(W + 1) - SB;
+    constexpr SlotList SL = wave_slots(W);
+    constexpr int NSW = SL.n;
     f32x16 acc[NSW];
 #pragma unroll
     for (int i = 0; i < NSW; ++i) acc[i] = f32x16{};
-    float z1r = 0.f;  // wave W_Z1: z1 of coordinate l
+    float z1r = 0.f;  // wave W_AUX: z1 of coordinate l
 
     // initial state: unit p
     if (MODE == MAIN) {
@@ -540,33 +673,27 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
       for (int i = 0; i < NSW; ++i)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 x = src[((SB + i) * 4 + q4) * 64];
+          const float4 x = src[(SL.s[i] * 4 + q4) * 64];
           acc[i][4 * q4 + 0] = x.x;
           acc[i][4 * q4 + 1] = x.y;
           acc[i][4 * q4 + 2] = x.z;
           acc[i][4 * q4 + 3] = x.w;
         }
-      if (W == W_Z1) z1r = reinterpret_cast<const float*>(unit_at(p) + Z1_F4)[l];
+      if (W == W_AUX) z1r = reinterpret_cast<const float*>(unit_at(p) + Z1_F4)[l];
     }
 
     // chunk loop: iteration i stages chunk i+1, computes chunk i and
     // finishes chunk i-1
-    ra[0] = load_a(0);
-    if (has_v) rvv[0] = load_v(0);
-    stage(0, 0, S0_{});
+    ra = load_a(0);
+    if (has_v) rvv = load_v(0);
+    stage(0, 0);
     __syncthreads();
-    auto iter = [&](int i, auto slot) __attribute__((always_inline)) {
-      stage(i + 1, (i + 1) & 1, slot);
+    for (int i = 0; i < nch; ++i) {
+      stage(i + 1, (i + 1) & 1);
       compute_w(wtag, acc, z1r, i, i & 1, want_out);
       if (want_out && i > 0) finalize(i - 1);
       __syncthreads();
-    };
-    int i = 0;
-    for (; i + 2 <= nch; i += 2) {
-      iter(i, S0_{});
-      iter(i + 1, S0_{});
     }
-    if (i < nch) iter(i, S0_{});
     if (want_out && nch > 0) finalize(nch - 1);
 
     // results
@@ -582,14 +709,14 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
       for (int sl = 0; sl < NSW; ++sl)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          dstu[((SB + sl) * 4 + q4) * 64 + l] =
+          dstu[(SL.s[sl] * 4 + q4) * 64 + l] =
               float4{acc[sl][4 * q4], acc[sl][4 * q4 + 1], acc[sl][4 * q4 + 2], acc[sl][4 * q4 + 3]};
-      if (W == W_Z1) {
+      if (W == W_AUX) {
         reinterpret_cast<float*>(dstu + Z1_F4)[l] = z1r;
         if (l == 0) dstu[Z0_F4] = float4{count, 0.f, 0.f, 0.f};
       }
     } else if (want_state) {
-      if (W == W_Z1 && hv == 0) {
+      if (W == W_AUX && hv == 0) {
         float* z = a.z + static_cast<size_t>(bh) * F;
         z[1 + l] = z1r;
         if (l == 0) z[0] = count;
@@ -597,7 +724,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
       const int col = DH * hv + lc;
       static_for<0, NSW>([&](auto sli) {
         constexpr int sl = decltype(sli)::value;
-        constexpr int s = SB + sl;
+        constexpr int s = SL.s[sl];
         constexpr Slot t = slot_info(s);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
