@@ -41,7 +41,10 @@
  *  - taylor_last_error() returns a message for the last non-OK status on the
  *    calling thread (thread-local; valid until the next call on that thread).
  *  - Supported (d, dv, n_terms): d = 16 with dv in {16, 64} and n_terms in
- *    {1, 3, 5}; d = 32 or 64 with dv in {16, 64} and n_terms in {1, 3}. n_terms must
+ *    {1, 3, 5}, and with dv = 64 and n_terms = 7 (order 6, F = 74,613: the
+ *    highest even order the positivity-floor README discusses, minimum
+ *    weight about 0.15); d = 32 or 64 with dv in {16, 64} and n_terms in
+ *    {1, 3}. The feature map supports the same (d, n_terms). n_terms must
  *    be odd so that the highest order is even and every weight is positive
  *    ("Two prerequisites" on the same page; posfloor README, "The 1/2
  *    positivity floor": even truncations are globally positive). Anything
@@ -123,7 +126,8 @@ size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_t
  *             scratch: clobbered by the call, never read before written.
  * B, H or N may be 0: then no token is processed; with N = 0 the final state
  * is S0 (or zero). The normalisation divides by a sum of weights that is
- * >= 1/2 per key for n_terms = 3 (>= 0.27 for 5), so it never divides by 0.
+ * >= 1/2 per key for n_terms = 3 (>= 0.27 for 5, >= 0.149 for 7), so it never
+ * divides by 0.
  * Range: several bf16 instantiations carry operands in fp16 (largest finite
  * magnitude 65504) with fp32 accumulation:
  *  - order 2, d = 16, dv = 64: keys, values, key products k_i k_j, and the
@@ -132,8 +136,10 @@ size_t taylor_attn_prefill_workspace(int B, int H, int N, int d, int dv, int n_t
  *  - order 2, d = 64: q/a, the query products q_i q_j / a^2, k_i k_j, values
  *    and the intra-chunk weights;
  *  - the other bf16 instantiations with n_terms > 1 and d > 16, or
- *    n_terms = 5, use keys halved, so the products of m halved coordinates
- *    (m <= 4) must stay below 65504, e.g. |k_i| < 32 for n_terms = 5.
+ *    n_terms = 5 or 7, use keys halved, so the products of m halved
+ *    coordinates must stay below 65504, e.g. |k_i| < 32 for n_terms = 5;
+ *    for n_terms = 7 the key features also carry the sqrt-multinomial
+ *    weight (at most sqrt(720) ~ 26.8), e.g. |k_i| < 8 suffices.
  * Under the normalisation the method asks for (|q.k/a| of order 1) these
  * always hold. Beyond them results are inf or NaN from the first affected
  * row on; rows of earlier queries stay exact, because the causal mask sets

@@ -20,14 +20,17 @@ taylor_status fail(taylor_status s, const std::string& msg) {
   return s;
 }
 
-bool supported(int d, int dv, int n_terms) {
-  if (dv != 16 && dv != 64) return false;
-  if (d == 16) return n_terms == 1 || n_terms == 3 || n_terms == 5;
+bool supported_dn(int d, int n_terms) {
+  if (d == 16) return n_terms == 1 || n_terms == 3 || n_terms == 5 || n_terms == 7;
   if (d == 32 || d == 64) return n_terms == 1 || n_terms == 3;
   return false;
 }
 
-bool supported_dn(int d, int n_terms) { return supported(d, 16, n_terms); }
+bool supported(int d, int dv, int n_terms) {
+  if (dv != 16 && dv != 64) return false;
+  if (n_terms == 7) return d == 16 && dv == 64;  // order 6: one instantiation
+  return supported_dn(d, n_terms);
+}
 
 taylor_status check_dn(int d, int dv, int n_terms, bool with_dv) {
   if (n_terms >= 1 && n_terms % 2 == 0)
@@ -39,7 +42,8 @@ taylor_status check_dn(int d, int dv, int n_terms, bool with_dv) {
                 "unsupported configuration d=" + std::to_string(d) +
                     (with_dv ? " dv=" + std::to_string(dv) : std::string()) +
                     " n_terms=" + std::to_string(n_terms) +
-                    " (supported: d=16 with n_terms 1,3,5; d=32 or 64 with n_terms 1,3; dv 16 or 64)");
+                    " (supported: d=16 with n_terms 1,3,5 and dv 16 or 64, or n_terms 7 and dv 64; d=32 or 64 with n_terms"
+                    " 1,3 and dv 16 or 64)");
   return TAYLOR_OK;
 }
 

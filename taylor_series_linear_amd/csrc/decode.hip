@@ -163,6 +163,182 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// 1/m! for the degrees of a decoded feature
+__device__ __forceinline__ float inv_factorial(int m) {
+  float r = 1.f;
+  for (int j = 2; j <= m; ++j) r *= 1.f / static_cast<float>(j);
+  return r;
+}
+
+// Decode step for bases too wide to hold phi(k) and alpha*phi(q) in LDS at
+// once (order 6 at d = 16: 74,613 features, a 19 MB state per head). The
+// state is processed in blocks of FB rows: every thread decodes the first
+// feature of its run of the block and steps through the run, writing both
+// feature values to LDS; then the block's rows stream exactly as in
+// decode_kernel (read, update, write back, fold into the read-out). The
+// first rows of a block are requested before its features are generated.
+template <int D, int DV, int NT, bool BF16>
+__global__ __launch_bounds__(256) void decode_wide_kernel(DecodeArgs a) {
+  constexpr int F = feature_count(D, NT);
+  constexpr int FB = 2048;                // state rows per block
+  constexpr int RUN = FB / 256;           // features generated per thread and block
+  constexpr int NQ = DV / 4;              // float4 columns per state row
+  constexpr int NG = 256 / NQ;            // row groups
+  constexpr int RPB = FB / NG;            // rows per row group and block
+  constexpr int BATCH = 8;                // rows in flight per thread
+  static_assert(RPB % BATCH == 0 && FB % 256 == 0, "block shape");
+
+  __shared__ float sq[D], sk[D];
+  __shared__ __attribute__((aligned(16))) float sv[DV];
+  __shared__ float sfk[FB], sfq[FB];
+  __shared__ f32x4 red[256];
+  __shared__ float dred[256];
+
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const float g = a.gamma;
+  const int dq = tid % NQ;
+  const int rg = tid / NQ;
+  float* Sh = a.S + static_cast<size_t>(bh) * F * DV;
+  float* zh = a.z + static_cast<size_t>(bh) * F;
+
+  f32x4 rows[BATCH];
+  auto load_batch = [&](int f0, int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int f = f0 + rg + NG * (r0 + j);
+      if (f < F)
+        rows[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + static_cast<size_t>(f) * DV + 4 * dq));
+    }
+  };
+  load_batch(0, 0);
+
+  if (tid < D) {
+    sq[tid] = load_in<BF16>(a.q, static_cast<size_t>(bh) * D + tid);
+    sk[tid] = load_in<BF16>(a.k, static_cast<size_t>(bh) * D + tid);
+  }
+  if (tid < DV) sv[tid] = load_in<BF16>(a.v, static_cast<size_t>(bh) * DV + tid);
+  __syncthreads();
+
+  // query/key preprocessing, as in decode_kernel
+  float fq = a.q_scale * (a.q_head_scale != nullptr ? a.q_head_scale[bh % a.H] : 1.f);
+  float fk = a.k_scale;
+  if (a.qk_norm) {
+    float nq = 0.f, nk = 0.f;
+    for (int j = 0; j < D; ++j) {
+      nq += sq[j] * sq[j];
+      nk += sk[j] * sk[j];
+    }
+    fq = nq > 0.f ? fq / __builtin_sqrtf(nq) : 0.f;
+    fk = nk > 0.f ? fk / __builtin_sqrtf(nk) : 0.f;
+  }
+  const float cq = fq * a.inv_a;
+
+  const f32x4 vv = *reinterpret_cast<const f32x4*>(sv + 4 * dq);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float dpart = 0.f;
+  for (int f0 = 0; f0 < F; f0 += FB) {
+    if (f0 > 0) {
+      __syncthreads();  // every thread is done with the previous block's features
+      load_batch(f0, 0);
+    }
+    RankedFeature e = rank_decode(D, NT, f0 + RUN * tid);
+#pragma unroll
+    for (int j = 0; j < RUN; ++j) {
+      float pk = 0.f, pq = 0.f;
+      if (f0 + RUN * tid + j < F) {
+        pk = e.w;
+        pq = e.w * inv_factorial(e.m);
+#pragma unroll
+        for (int u = 0; u < kMaxOrderRank; ++u) {
+          if (u < e.m) {
+            pk *= sk[e.idx[u]] * fk;
+            pq *= sq[e.idx[u]] * cq;
+          }
+        }
+      }
+      sfk[RUN * tid + j] = pk;
+      sfq[RUN * tid + j] = pq;
+      if (j + 1 < RUN) rank_next(D, e);
+    }
+    __syncthreads();
+    for (int r0 = 0; r0 < RPB; r0 += BATCH) {
+      if (r0 > 0) load_batch(f0, r0);
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int fl = rg + NG * (r0 + j);
+        if (f0 + fl < F) {
+          const f32x4 s = rows[j] * g + sfk[fl] * vv;
+          __builtin_nontemporal_store(s, reinterpret_cast<f32x4*>(Sh + static_cast<size_t>(f0 + fl) * DV + 4 * dq));
+          acc += sfq[fl] * s;
+        }
+      }
+    }
+    float zv[FB / 256];
+#pragma unroll
+    for (int j = 0; j < FB / 256; ++j) {
+      const int f = f0 + tid + 256 * j;
+      zv[j] = f < F ? __builtin_nontemporal_load(zh + f) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < FB / 256; ++j) {
+      const int fl = tid + 256 * j;
+      if (f0 + fl < F) {
+        const float zz = zv[j] * g + sfk[fl];
+        __builtin_nontemporal_store(zz, zh + f0 + fl);
+        dpart += sfq[fl] * zz;
+      }
+    }
+  }
+  red[tid] = acc;
+  dred[tid] = dpart;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) dred[tid] += dred[tid + s];
+    __syncthreads();
+  }
+  if (tid < NQ) {
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int gg = 0; gg < NG; ++gg) num += red[gg * NQ + tid];
+    const float r = 1.f / dred[0];
+    const size_t off = static_cast<size_t>(bh) * DV + 4 * tid;
+    if (a.out_bf16) {
+      bf16x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(num[i] * r);
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = num * r;
+    }
+  }
+}
+
+// Feature map of a basis without a compile-time table: each thread writes a
+// run of RUN consecutive features of one row, decoding the first and
+// stepping through the rest.
+template <int D, int NT, bool BF16>
+__global__ __launch_bounds__(256) void feature_map_wide_kernel(const void* x, int64_t rows, float* phi,
+                                                               OrderScale sc) {
+  constexpr int F = feature_count(D, NT);
+  constexpr int RUN = 16;
+  constexpr int RPR = (F + RUN - 1) / RUN;  // runs per row
+  const int64_t total = rows * RPR;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t r = u / RPR;
+    const int f0 = static_cast<int>(u - r * RPR) * RUN;
+    RankedFeature e = rank_decode(D, NT, f0);
+    for (int j = 0; j < RUN && f0 + j < F; ++j) {
+      float v = e.w * sc.s[e.m];
+#pragma unroll
+      for (int t = 0; t < kMaxOrderRank; ++t)
+        if (t < e.m) v *= load_in<BF16>(x, static_cast<size_t>(r) * D + e.idx[t]);
+      phi[r * F + f0 + j] = v;
+      rank_next(D, e);
+    }
+  }
+}
+
 // phi[row, f] = w_f * prod_j x[row, i_j] * scale[m_f]
 template <int D, int NT, bool BF16>
 __global__ __launch_bounds__(256) void feature_map_kernel(const void* x, int64_t rows, float* phi,
@@ -214,6 +390,14 @@ hipError_t decode_launch(int d, int dv, int n_terms, bool bf16, const DecodeArgs
   }
   TL_DECODE_CFGS(X)
 #undef X
+  // bases too wide for the LDS-resident features
+  if (d == 16 && dv == 64 && n_terms == 7) {
+    if (bf16)
+      hipLaunchKernelGGL((decode_wide_kernel<16, 64, 7, true>), dim3(a.BH), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_wide_kernel<16, 64, 7, false>), dim3(a.BH), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
@@ -234,6 +418,16 @@ hipError_t feature_map_launch(int d, int n_terms, bool bf16, const void* x, int6
   }
   X(16, 1) X(16, 3) X(16, 5) X(32, 1) X(32, 3) X(64, 1) X(64, 3)
 #undef X
+  if (d == 16 && n_terms == 7) {
+    constexpr int F = feature_count(16, 7);
+    const int64_t runs = rows * ((F + 15) / 16);
+    const unsigned wb = static_cast<unsigned>((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
+    if (bf16)
+      hipLaunchKernelGGL((feature_map_wide_kernel<16, 7, true>), dim3(wb), dim3(256), 0, stream, x, rows, phi, sc);
+    else
+      hipLaunchKernelGGL((feature_map_wide_kernel<16, 7, false>), dim3(wb), dim3(256), 0, stream, x, rows, phi, sc);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 

@@ -10,6 +10,8 @@
 
 #include <stdint.h>
 
+#include "rank.hpp"
+
 namespace tl {
 
 constexpr int kMaxOrder = 4;  // highest degree instantiated (n_terms <= 5)

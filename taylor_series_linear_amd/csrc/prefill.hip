@@ -99,6 +99,11 @@ struct PCfg {
   // query and the key side (1, the coordinates, and for orders above 2 the
   // pair products), token-contiguous
   static constexpr bool PAIRS = NT > 3;
+  // orders 5 and 6 are products of three table entries; their features are
+  // decoded at run time (no compile-time basis table) and the key side
+  // carries the sqrt-multinomial weight, so that internal and canonical
+  // state rows differ by KS^m only
+  static constexpr bool TRIPLE = NT > 5;
   static constexpr int TE = UNROLL ? 0 : 1 + D + (PAIRS ? D * (D + 1) / 2 : 0);
   static constexpr int TP = C + 4;
   // key side of the table-driven generator: bf16 inputs keep the key table,
@@ -111,7 +116,8 @@ struct PCfg {
   static constexpr int OFF_TQ = OFF_DEN + C * 4;
   static constexpr int OFF_TK = OFF_TQ + TE * TP * 4;
   static constexpr int LDS = OFF_TK + TE * TPK * KES;
-  static_assert(NT <= 5, "features are products of two table entries up to order 4");
+  static_assert(NT <= 7, "features are products of at most three table entries (order 6)");
+  static_assert(!TRIPLE || (PAIRS && !UNROLL), "orders 5 and 6 use the table-driven generator with pairs");
   static_assert(FS % 32 == 0 && C % 32 == 0 && DV % 16 == 0, "tile multiples");
   static_assert(D % 16 == 0, "head dim multiple of 16");
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -230,9 +236,12 @@ __device__ const PackedTable<D, NT> g_ptab = make_packed<D, NT>();
 // (i <= j, lexicographic; orders above 2 only)] times a constant:
 //   m = 0: T[0] T[0],  m = 1: T[0] T[1+i],  m = 2: T[0] T[pair(i,j)] (or
 //   T[1+i] T[1+j] without pairs),  m = 3: T[pair(i,j)] T[1+k],
-//   m = 4: T[pair(i,j)] T[pair(k,l)].
+//   m = 4: T[pair(i,j)] T[pair(k,l)],
+// and with a third entry (bases up to order 6)
+//   m = 5: T[pair(i,j)] T[pair(k,l)] T[1+p],  m = 6: three pairs,
+// the third entry being T[0] = 1 for lower orders.
 // The tables are built once per chunk; each lane owns a feature and reads
-// both of its rows 16 bytes at a time.
+// its rows 16 bytes at a time.
 template <int D>
 __host__ __device__ constexpr int tab_pair(int i, int j) {
   return 1 + D + i * D - i * (i - 1) / 2 + (j - i);
@@ -244,20 +253,34 @@ __host__ __device__ constexpr int tab_pair(int i, int j) {
 // the canonical one. Internal states relate to canonical ones by
 // canonical = (w / KS^m) internal.
 struct TabFeat {
-  int oa, ob;  // offsets (elements) of the two table rows, query table
-  int ka, kb;  // the same rows in the key table
-  float cq;    // query-side weight
+  int oa, ob, oc;  // offsets (elements) of the table rows, query table (oc: third entry)
+  int ka, kb, kc;  // the same rows in the key table
+  float cq;        // query-side weight
+  float ck;        // key-side weight (bases with three-entry features; 1 otherwise)
 };
 
 template <class Cfg>
 __device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
   constexpr int D = Cfg::D, TP = Cfg::TP;
-  TabFeat t{0, 0, 0, 0, 0.f};
+  TabFeat t{0, 0, 0, 0, 0, 0, 0.f, 0.f};
   if (f >= Cfg::F) return t;
-  const PackedFeature e = g_ptab<D, Cfg::NT>.e[f];
-  const int m = static_cast<int>(e.m);
-  const int i0 = e.idx & 255, i1 = (e.idx >> 8) & 255, i2 = (e.idx >> 16) & 255, i3 = e.idx >> 24;
-  int a = 0, b = 0;
+  int m, i0, i1, i2, i3, i4 = 0, i5 = 0;
+  float w, inv_mfact;
+  if constexpr (Cfg::TRIPLE) {
+    const RankedFeature e = rank_decode(D, Cfg::NT, f);
+    m = e.m;
+    i0 = e.idx[0], i1 = e.idx[1], i2 = e.idx[2], i3 = e.idx[3], i4 = e.idx[4], i5 = e.idx[5];
+    w = e.w;
+    inv_mfact = 1.f;
+    for (int j = 2; j <= m; ++j) inv_mfact *= 1.f / static_cast<float>(j);
+  } else {
+    const PackedFeature e = g_ptab<D, Cfg::NT>.e[f];
+    m = static_cast<int>(e.m);
+    i0 = e.idx & 255, i1 = (e.idx >> 8) & 255, i2 = (e.idx >> 16) & 255, i3 = e.idx >> 24;
+    w = e.w;
+    inv_mfact = e.inv_mfact;
+  }
+  int a = 0, b = 0, c = 0;
   if (m == 1) {
     b = 1 + i0;
   } else if (m == 2) {
@@ -273,14 +296,27 @@ __device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
   } else if (m == 4) {
     a = tab_pair<D>(i0, i1);
     b = tab_pair<D>(i2, i3);
+  } else if (m == 5) {
+    a = tab_pair<D>(i0, i1);
+    b = tab_pair<D>(i2, i3);
+    c = 1 + i4;
+  } else if (m == 6) {
+    a = tab_pair<D>(i0, i1);
+    b = tab_pair<D>(i2, i3);
+    c = tab_pair<D>(i4, i5);
   }
   t.oa = a * TP;
   t.ob = b * TP;
+  t.oc = c * TP;
   t.ka = a * Cfg::TPK;
   t.kb = b * Cfg::TPK;
-  float cq = e.w * e.w * e.inv_mfact;
+  t.kc = c * Cfg::TPK;
+  // three-entry bases: key side w u(KS k), query side w alpha_m / KS^m;
+  // otherwise key side u(KS k), query side w^2 alpha_m / KS^m
+  float cq = (Cfg::TRIPLE ? w : w * w) * inv_mfact;
   for (int j = 0; j < m; ++j) cq *= inv_a / Cfg::KS;
   t.cq = cq;
+  t.ck = Cfg::TRIPLE ? w : 1.f;
   return t;
 }
 
@@ -290,6 +326,17 @@ template <class Cfg>
 __device__ __forceinline__ float state_scale(int f) {
   if constexpr (Cfg::UNROLL) {
     return 1.f;
+  } else if constexpr (Cfg::TRIPLE) {
+    // internal rows carry w KS^m: canonical = internal / KS^m
+    int m = 0;
+    long long end = 1;
+    while (m + 1 < Cfg::NT && f >= end) {
+      ++m;
+      end += rank_binom(Cfg::D + m - 1, m);
+    }
+    float sc = 1.f;
+    for (int j = 0; j < m; ++j) sc *= 1.f / Cfg::KS;
+    return sc;
   } else {
     const PackedFeature e = g_ptab<Cfg::D, Cfg::NT>.e[f];
     float sc = e.w;
@@ -389,96 +436,41 @@ __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, cons
     if constexpr (QSIDE) {
       const float* __restrict__ ta = T + tf[j].oa;
       const float* __restrict__ tb = T + tf[j].ob;
+      const float* __restrict__ tc = T + tf[j].oc;
       const float cf = tf[j].cq;
 #pragma unroll
       for (int t0 = 0; t0 < C; t0 += 4) {
         const f32x4 va = *reinterpret_cast<const f32x4*>(ta + t0);
-        const f32x4 vb = *reinterpret_cast<const f32x4*>(tb + t0);
+        f32x4 vb = *reinterpret_cast<const f32x4*>(tb + t0);
+        if constexpr (Cfg::TRIPLE) vb *= *reinterpret_cast<const f32x4*>(tc + t0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) dst[(t0 + u) * Cfg::PQ + fl] = Cfg::M::cvt(va[u] * vb[u] * cf);
       }
     } else if constexpr (Cfg::KH) {
       const TE_* ta = T + tf[j].ka;
       const TE_* tb = T + tf[j].kb;
+      const TE_* tc = T + tf[j].kc;
+      const _Float16 ck = static_cast<_Float16>(tf[j].ck);
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 8)
-        *reinterpret_cast<f16x8*>(dst + fl * Cfg::PK + t0) =
-            *reinterpret_cast<const f16x8*>(ta + t0) * *reinterpret_cast<const f16x8*>(tb + t0);
+      for (int t0 = 0; t0 < C; t0 += 8) {
+        f16x8 v = *reinterpret_cast<const f16x8*>(ta + t0) * *reinterpret_cast<const f16x8*>(tb + t0);
+        if constexpr (Cfg::TRIPLE) v = v * (*reinterpret_cast<const f16x8*>(tc + t0) * ck);
+        *reinterpret_cast<f16x8*>(dst + fl * Cfg::PK + t0) = v;
+      }
     } else {
       const TE_* ta = T + tf[j].ka;
       const TE_* tb = T + tf[j].kb;
+      const TE_* tc = T + tf[j].kc;
+      const float ck = tf[j].ck;
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 4)
-        *reinterpret_cast<f32x4*>(dst + fl * Cfg::PK + t0) =
-            *reinterpret_cast<const f32x4*>(ta + t0) * *reinterpret_cast<const f32x4*>(tb + t0);
-    }
-  }
-}
-
-// Lanes own features, loop over the chunk's tokens; x rows are read from LDS
-// (all lanes read the same row: broadcast).
-template <class Cfg, bool QSIDE>
-__device__ __forceinline__ void gen_table(int w, int lane, int f0, const typename Cfg::E* X,
-                                          typename Cfg::E* dst, float inv_a) {
-  using E = typename Cfg::E;
-  constexpr int NB = (Cfg::FS + 63) / 64;
-  const auto& tab = g_ptab<Cfg::D, Cfg::NT>;
-  for (int blk = w; blk < NB; blk += Cfg::NW) {
-    const int fl = 64 * blk + lane;
-    if (fl >= Cfg::FS) continue;
-    const int f = f0 + fl;
-    float cf = 0.f;
-    uint32_t idx = 0;
-    int m = 0;
-    if (f < Cfg::F) {
-      const PackedFeature e = tab.e[f];
-      idx = e.idx;
-      m = static_cast<int>(e.m);
-      cf = e.w;
-      if (QSIDE) {
-        cf *= e.inv_mfact;
-        for (int j = 0; j < m; ++j) cf *= inv_a;
-      }
-    }
-    const int i0 = idx & 255, i1 = (idx >> 8) & 255, i2 = (idx >> 16) & 255, i3 = idx >> 24;
-    if constexpr (QSIDE) {
-      for (int t = 0; t < Cfg::C; ++t) {
-        const E* xr = X + t * Cfg::XP;
-        float v = cf;
-        if (m > 0) v *= static_cast<float>(xr[i0]);
-        if (m > 1) v *= static_cast<float>(xr[i1]);
-        if (m > 2) v *= static_cast<float>(xr[i2]);
-        if (m > 3) v *= static_cast<float>(xr[i3]);
-        dst[t * Cfg::PQ + fl] = Cfg::M::cvt(v);
-      }
-    } else {
-      for (int t0 = 0; t0 < Cfg::C; t0 += 8) {
-        E vals[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const E* xr = X + (t0 + j) * Cfg::XP;
-          float v = cf;
-          if (m > 0) v *= static_cast<float>(xr[i0]);
-          if (m > 1) v *= static_cast<float>(xr[i1]);
-          if (m > 2) v *= static_cast<float>(xr[i2]);
-          if (m > 3) v *= static_cast<float>(xr[i3]);
-          vals[j] = Cfg::M::cvt(v);
-        }
-        E* out = dst + fl * Cfg::PK + t0;
-        if constexpr (Cfg::BF16) {
-          bf16x8 pk;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pk[j] = vals[j];
-          *reinterpret_cast<bf16x8*>(out) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>(out) = f32x4{vals[0], vals[1], vals[2], vals[3]};
-          *reinterpret_cast<f32x4*>(out + 4) = f32x4{vals[4], vals[5], vals[6], vals[7]};
-        }
+      for (int t0 = 0; t0 < C; t0 += 4) {
+        f32x4 v = *reinterpret_cast<const f32x4*>(ta + t0) * *reinterpret_cast<const f32x4*>(tb + t0);
+        if constexpr (Cfg::TRIPLE) v = v * (*reinterpret_cast<const f32x4*>(tc + t0) * ck);
+        *reinterpret_cast<f32x4*>(dst + fl * Cfg::PK + t0) = v;
       }
     }
   }
 }
-
 
 // Score tiles of one chunk handled by wave R (tiles R, R+NW, ...): all
 // operand fragments are fetched first, then the MFMAs run, then the
@@ -1134,6 +1126,8 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(16, 16, 5, false, 256, 32, false)       \
   X(16, 64, 5, true, 608, 32, false)        \
   X(16, 64, 5, false, 256, 32, false)       \
+  X(16, 64, 7, true, 608, 32, false)        \
+  X(16, 64, 7, false, 256, 32, false)       \
   X(32, 16, 1, true, 32, 64, true)          \
   X(32, 16, 1, false, 32, 64, true)         \
   X(32, 64, 1, true, 32, 64, true)          \

@@ -6,10 +6,12 @@
 
 #include <stdint.h>
 
+#ifndef TL_HD
 #ifdef __HIPCC__
 #define TL_HD __host__ __device__
 #else
 #define TL_HD
+#endif
 #endif
 
 namespace tl {

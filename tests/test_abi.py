@@ -28,7 +28,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_feature_dim():
-    for d, n, F in [(16, 3, 153), (16, 5, 4845), (64, 3, 2145), (16, 1, 1), (1, 4, 4)]:
+    for d, n, F in [(16, 3, 153), (16, 5, 4845), (64, 3, 2145), (16, 7, 74613), (16, 1, 1), (1, 4, 4)]:
         assert L.taylor_feature_dim(d, n) == F == math.comb(d + n - 1, n - 1)
     assert L.taylor_feature_dim(0, 3) == -1
     assert L.taylor_feature_dim(16, 0) == -1
@@ -36,10 +36,10 @@ def test_feature_dim():
 
 def test_supported_set():
     ok = {(16, dv, n) for dv in (16, 64) for n in (1, 3, 5)} | {(dd, dv, n) for dd in (32, 64) for dv in (16, 64)
-                                                                for n in (1, 3)}
+                                                                for n in (1, 3)} | {(16, 64, 7)}
     for d in (8, 16, 32, 64):
         for dv in (8, 16, 32, 64, 128):
-            for n in range(0, 7):
+            for n in range(0, 10):
                 assert bool(L.taylor_is_supported(d, dv, n)) == ((d, dv, n) in ok)
 
 

@@ -33,7 +33,8 @@ def rel(a, b):
 # Feature map: multinomial theorem and tensor-power identity (C-P1)
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("d,m", [(1, 3), (3, 2), (4, 3), (5, 4), (16, 2), (16, 4), (64, 2)])
+@pytest.mark.parametrize("d,m", [(1, 3), (3, 2), (4, 3), (5, 4), (16, 2), (16, 4), (64, 2), (3, 6), (4, 5),
+                                 (16, 6)])
 def test_phi_block_dot_is_power_of_dot(d, m):
     rng = np.random.default_rng(d * 10 + m)
     x = rng.standard_normal((7, d))
@@ -46,7 +47,7 @@ def test_phi_block_dot_is_power_of_dot(d, m):
     assert np.max(np.abs(px @ py.T - want)) <= 1e-12 * np.max(np.abs(want)) + 1e-300
 
 
-@pytest.mark.parametrize("d,m", [(2, 2), (3, 3), (4, 2), (3, 4)])
+@pytest.mark.parametrize("d,m", [(2, 2), (3, 3), (4, 2), (3, 4), (2, 6), (3, 5)])
 def test_phi_matches_full_tensor_power(d, m):
     # <x^{(x)m}, y^{(x)m}> built from explicit Kronecker powers.
     rng = np.random.default_rng(99 + d + m)
@@ -127,6 +128,10 @@ def test_widths():
         assert T.n_features(d, n) == F
         assert math.comb(d + n - 1, n - 1) == F  # hockey-stick closed form
         assert T.phi(np.ones((1, d)), n).shape[1] == F
+    # order 6 at d = 16 (the highest even order of the positivity-floor
+    # README's minima): the width by brute-force enumeration of the basis
+    F6 = sum(sum(1 for _ in itertools.combinations_with_replacement(range(16), m)) for m in range(7))
+    assert F6 == T.n_features(16, 7) == math.comb(22, 6) == 74613
     cap = gold("posfloor_printed.json")["gram_capacity"]
     d = cap["d"]
     assert (d + 1) * (d + 2) // 2 == cap["value"] == T.n_features(d, 3)
@@ -156,6 +161,26 @@ def test_state_rank(case):
         tp = np.stack([tpow(kk) for kk in K])
         s2 = np.linalg.svd(tp, compute_uv=False)
         assert int(np.sum(s2 > s2[0] * 1e-10)) == r
+
+
+@pytest.mark.parametrize("d,m", [(3, 6), (4, 5), (2, 6)])
+def test_state_rank_high_orders(d, m):
+    # "Higher orders": the rank of the order-m key features (and of the full
+    # tensor power) is C(d+m-1, m), for the orders 5 and 6 as well
+    r = math.comb(d + m - 1, m)
+    rng = np.random.default_rng(17 + d + m)
+    K = rng.standard_normal((3 * r, d))
+    lo, hi = T.n_features(d, m), T.n_features(d, m + 1)
+    s = np.linalg.svd(T.phi(K, m + 1)[:, lo:hi], compute_uv=False)
+    assert hi - lo == r and int(np.sum(s > s[0] * 1e-10)) == r
+
+    def tpow(x):
+        out = np.ones(1)
+        for _ in range(m):
+            out = np.kron(out, x)
+        return out
+    s2 = np.linalg.svd(np.stack([tpow(kk) for kk in K]), compute_uv=False)
+    assert int(np.sum(s2 > s2[0] * 1e-10)) == r
 
 
 def test_rank_truncation_breaks_readout():
