@@ -753,6 +753,257 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   }
 }
 
+// Segment sums (update only) of segments 0..P-2, written to unit p + 1 of
+// both value halves of the head. Here the features, not the value columns,
+// are split over the two workgroups of a (head, segment): each holds its
+// state tiles for all 64 value columns, so every key-product fragment feeds
+// two matrix-core products (one per value half) and the key rows are read
+// once per pair of tiles. 64 tokens are staged per barrier.
+namespace fs {
+constexpr int C = 64;                    // tokens per stage
+constexpr int KTP = C + 8;               // K'^T rows (fp16): coordinates 0..63, then 0..31 again
+constexpr int VTP = C + 8;               // V^T rows (fp16), all 64 value columns
+constexpr int KT = 0;
+constexpr int VT = KT + 96 * KTP * 2;
+constexpr int BUF = VT + DV * VTP * 2;
+static_assert(2 * BUF <= 160 * 1024 && VT % 16 == 0 && BUF % 16 == 0 && (KTP * 2) % 16 == 0, "LDS layout");
+
+// Work of wave w of the workgroup holding feature half f: up to five state
+// slots (each a tile per value half; key rows of first range AB = 32 f),
+// at most one Gram tile, and (one wave) the key sums z1.
+constexpr int MAXC = 5;
+struct Work {
+  int nc;
+  int cls[MAXC];  // state slots 0..67
+  int gram;       // Gram slot 68..70, or -1
+  bool z1;
+};
+__host__ __device__ constexpr Work work(int f, int w) {
+  if (f == 0) {
+    // pair classes of the first range 0..31 and the linear tile of range 0
+    if (w == NW - 1) return Work{5, {4 * w, 4 * w + 1, 4 * w + 2, 4 * w + 3, 65}, -1, false};
+    return Work{4, {4 * w, 4 * w + 1, 4 * w + 2, 4 * w + 3, -1}, -1, false};
+  }
+  // pair classes of the range 32..63; the (r, r + 32) class, the second
+  // linear tile, the constant, the Gram tiles and z1 on top
+  const int b = 32 + 4 * w;
+  if (w < 3) return Work{5, {b, b + 1, b + 2, b + 3, w == 0 ? 64 : (w == 1 ? 66 : 67)}, -1, false};
+  if (w < 6) return Work{4, {b, b + 1, b + 2, b + 3, -1}, 68 + (w - 3), false};
+  return Work{4, {b, b + 1, b + 2, b + 3, -1}, -1, w == 6};
+}
+constexpr bool work_partitioned() {
+  int hits[NSLOT] = {};
+  int z1 = 0;
+  for (int f = 0; f < 2; ++f)
+    for (int w = 0; w < NW; ++w) {
+      const Work k = work(f, w);
+      for (int i = 0; i < k.nc; ++i) {
+        const int s = k.cls[i];
+        if (s < 0 || s >= NS) return false;
+        ++hits[s];
+        const Slot t = slot_info(s);
+        // pair classes and linear tiles use the workgroup's key range
+        if ((t.kind == S_CLASS && s != 64) || t.kind == S_LIN)
+          if (t.abase != 32 * f) return false;
+      }
+      if (k.gram >= 0) {
+        if (k.gram < NS || k.gram >= NSLOT) return false;
+        ++hits[k.gram];
+      }
+      z1 += k.z1 ? 1 : 0;
+    }
+  for (int s = 0; s < NSLOT; ++s)
+    if (hits[s] != 1) return false;
+  return z1 == 1;
+}
+static_assert(work_partitioned(), "every slot on exactly one wave of one feature half; z1 once");
+}  // namespace fs
+
+__global__ __launch_bounds__(NTHR, 1) void w2_segsum_fs(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * fs::BUF];
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lc = l & 31, lh = l >> 5;
+  const int PL = a.P - 1;
+  const int unit = blockIdx.x;
+  if (unit >= a.BH * 2 * PL) return;
+  const int bhf = unit / PL, p = unit - bhf * PL;
+  const int bh = bhf >> 1, f = bhf & 1;
+  const int N = a.N;
+  const int t0 = p * a.L;
+  const int t1 = min(N, t0 + a.L);
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  const int nst = (t1 - t0 + fs::C - 1) / fs::C;
+
+  auto kt = [&](int b) __attribute__((always_inline)) {
+    return reinterpret_cast<_Float16*>(smem + b * fs::BUF + fs::KT);
+  };
+  auto vt = [&](int b) __attribute__((always_inline)) {
+    return reinterpret_cast<_Float16*>(smem + b * fs::BUF + fs::VT);
+  };
+  const __bf16* kh = reinterpret_cast<const __bf16*>(a.k) + (static_cast<size_t>(bh) * N + t0) * D;
+  const __bf16* vh = reinterpret_cast<const __bf16*>(a.v) + (static_cast<size_t>(bh) * N + t0) * DV;
+  const auto rk = make_rsrc(kh, seg_rows * D * 2);
+  const auto rv = make_rsrc(vh, seg_rows * DV * 2);
+
+  // Staging: threads 0..255 hold a K item, 256..511 a V item: coordinates
+  // (or columns) 8 ic8 .. + 8 of the token pair 2 tp, 2 tp + 1. The pair is
+  // written to the transposed tile as one dword per coordinate. Rows past
+  // the segment's end load as zero (buffer range), so they add nothing.
+  const bool is_k = __builtin_amdgcn_readfirstlane(tid) < 256;
+  const int it = tid & 255, ic8 = it >> 5, tp = it & 31;
+  const auto rsrc = is_k ? rk : rv;
+  uint4 r0, r1;
+  auto load = [&](int c) __attribute__((always_inline)) {
+    const int row = c * fs::C + 2 * tp;
+    const uint32_t ra = static_cast<uint32_t>(row < static_cast<int>(seg_rows) ? row : static_cast<int>(seg_rows));
+    const uint32_t rb =
+        static_cast<uint32_t>(row + 1 < static_cast<int>(seg_rows) ? row + 1 : static_cast<int>(seg_rows));
+    r0 = bload16(rsrc, (ra * 64 + 8 * ic8) * 2);  // D == DV == 64
+    r1 = bload16(rsrc, (rb * 64 + 8 * ic8) * 2);
+  };
+  auto stage = [&](int b) __attribute__((always_inline)) {
+    const f16x8 x0 = b2h(__builtin_bit_cast(bf16x8, r0));
+    const f16x8 x1 = b2h(__builtin_bit_cast(bf16x8, r1));
+    _Float16* t = is_k ? kt(b) : vt(b);
+    const int pitch = is_k ? fs::KTP : fs::VTP;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<f16x2*>(t + (8 * ic8 + u) * pitch + 2 * tp) = f16x2{x0[u], x1[u]};
+    if (is_k && ic8 < 4) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) *reinterpret_cast<f16x2*>(t + (D + 8 * ic8 + u) * pitch + 2 * tp) = f16x2{x0[u], x1[u]};
+    }
+  };
+
+  auto wave_body = [&](auto ftag, auto wtag) __attribute__((always_inline)) {
+    constexpr int FH = decltype(ftag)::value;
+    constexpr int W = decltype(wtag)::value;
+    constexpr fs::Work WK = fs::work(FH, W);
+    constexpr int NC = WK.nc;
+    constexpr int AB = 32 * FH;  // first key range of the workgroup
+    constexpr bool HAS_G = WK.gram >= 0;
+    // the auxiliary key range (coordinates 32 (1 - FH) + lc) is needed by the
+    // (r, r + 32) class and by Gram tiles that touch it
+    constexpr bool NEED_OTHER = [] {
+      for (int i = 0; i < WK.nc; ++i)
+        if (WK.cls[i] == 64) return true;
+      if (WK.gram >= 0) {
+        const Slot g = slot_info(WK.gram);
+        if (32 * g.zr != 32 * FH || 32 * g.zc != 32 * FH) return true;
+      }
+      return false;
+    }();
+    f32x16 acc[2 * NC + (HAS_G ? 1 : 0)];
+#pragma unroll
+    for (int i = 0; i < 2 * NC + (HAS_G ? 1 : 0); ++i) acc[i] = f32x16{};
+    float z1r = 0.f;
+    auto chunk = [&](int b) __attribute__((always_inline)) {
+      const _Float16* K = kt(b);
+      const _Float16* V = vt(b);
+#pragma unroll
+      for (int ks = 0; ks < fs::C / 16; ++ks) {
+        const int col = 16 * ks + 8 * lh;
+        const f16x8 bv0 = lds<f16x8>(V + lc * fs::VTP + col);
+        const f16x8 bv1 = lds<f16x8>(V + (32 + lc) * fs::VTP + col);
+        const f16x8 kx = lds<f16x8>(K + (AB + lc) * fs::KTP + col);
+        f16x8 ko = kx;
+        if constexpr (NEED_OTHER) ko = lds<f16x8>(K + (32 - AB + lc) * fs::KTP + col);
+        static_for<0, NC>([&](auto ci) {
+          constexpr int i = decltype(ci)::value;
+          constexpr int s = WK.cls[i];
+          constexpr Slot t = slot_info(s);
+          f16x8 x;
+          if constexpr (s == 64) {
+            x = FH == 0 ? kx * ko : ko * kx;  // rows r and r + 32
+          } else if constexpr (t.kind == S_CLASS) {
+            x = kx * lds<f16x8>(K + (AB + t.koff + lc) * fs::KTP + col);
+          } else if constexpr (t.kind == S_LIN) {
+            x = kx;
+          } else {  // the constant
+            const _Float16 one = static_cast<_Float16>(lc == 0 ? 1.f : 0.f);
+            x = f16x8{one, one, one, one, one, one, one, one};
+          }
+          acc[2 * i] = mfma32h(x, bv0, acc[2 * i]);
+          acc[2 * i + 1] = mfma32h(x, bv1, acc[2 * i + 1]);
+        });
+        if constexpr (HAS_G) {
+          constexpr Slot g = slot_info(WK.gram);
+          const f16x8 xr = 32 * g.zr == AB ? kx : ko;
+          const f16x8 xc = 32 * g.zc == AB ? kx : ko;
+          acc[2 * NC] = mfma32h(xr, xc, acc[2 * NC]);
+        }
+      }
+      if constexpr (WK.z1) {
+        // z1 += keys (lane l = coordinate l), summed with fp16 dot2
+        const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+        const _Float16* kr0 = K + l * fs::KTP;
+        float zs = 0.f;
+#pragma unroll
+        for (int u = 0; u < fs::C / 8; ++u) {
+          const f16x8 x = lds<f16x8>(kr0 + 8 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) zs = __builtin_amdgcn_fdot2(f16x2{x[2 * e], x[2 * e + 1]}, ones, zs, false);
+        }
+        z1r += zs;
+      }
+    };
+    load(0);
+    stage(0);
+    load(1);
+    __syncthreads();
+    for (int c = 0; c < nst; ++c) {
+      if (c + 1 < nst) stage((c + 1) & 1);
+      load(c + 2);
+      chunk(c & 1);
+      __syncthreads();
+    }
+    // results: unit p + 1 of both value halves
+    float4* dst[2];
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+      dst[hv] = reinterpret_cast<float4*>(a.seg) + (static_cast<size_t>(bh * 2 + hv) * a.P + p + 1) * UNIT_F4;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          dst[hv][(WK.cls[i] * 4 + q4) * 64 + l] = float4{acc[2 * i + hv][4 * q4], acc[2 * i + hv][4 * q4 + 1],
+                                                           acc[2 * i + hv][4 * q4 + 2], acc[2 * i + hv][4 * q4 + 3]};
+    if constexpr (HAS_G) {
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          dst[hv][(WK.gram * 4 + q4) * 64 + l] = float4{acc[2 * NC][4 * q4], acc[2 * NC][4 * q4 + 1],
+                                                         acc[2 * NC][4 * q4 + 2], acc[2 * NC][4 * q4 + 3]};
+    }
+    if constexpr (WK.z1) {
+#pragma unroll
+      for (int hv = 0; hv < 2; ++hv) {
+        reinterpret_cast<float*>(dst[hv] + Z1_F4)[l] = z1r;
+        if (l == 0) dst[hv][Z0_F4] = float4{static_cast<float>(t1 - t0), 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  auto per_wave = [&](auto ftag) __attribute__((always_inline)) {
+    switch (w) {
+      case 0: wave_body(ftag, std::integral_constant<int, 0>{}); break;
+      case 1: wave_body(ftag, std::integral_constant<int, 1>{}); break;
+      case 2: wave_body(ftag, std::integral_constant<int, 2>{}); break;
+      case 3: wave_body(ftag, std::integral_constant<int, 3>{}); break;
+      case 4: wave_body(ftag, std::integral_constant<int, 4>{}); break;
+      case 5: wave_body(ftag, std::integral_constant<int, 5>{}); break;
+      case 6: wave_body(ftag, std::integral_constant<int, 6>{}); break;
+      default: wave_body(ftag, std::integral_constant<int, 7>{}); break;
+    }
+  };
+  if (f == 0)
+    per_wave(std::integral_constant<int, 0>{});
+  else
+    per_wave(std::integral_constant<int, 1>{});
+}
+
 // Unit 0 of each (head, half): S0/z0 in the internal layout (zeros without
 // an initial state). One workgroup of 64 threads per (head, half, slot), plus
 // one per (head, half) for z1 and z0.
@@ -885,7 +1136,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(w2_s0_unit, dim3(a.BH * 2 * (NSLOT + 1)), dim3(64), 0, stream, a.S0, a.z0, seg, a.P);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.P > 1) {
-    hipLaunchKernelGGL((w2_kernel<SEGSUM, true>), dim3(a.BH * 2 * (a.P - 1)), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL(w2_segsum_fs, dim3(a.BH * 2 * (a.P - 1)), dim3(NTHR), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = static_cast<int64_t>(a.BH) * 2 * UNIT_F4;
     hipLaunchKernelGGL(w2_scan, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, seg, a.BH * 2,
