@@ -276,6 +276,16 @@ def bench_decode(args, torch, tl, W):
     ms_hot = time_loop(hot, w.steps, torch)
     F = feature_dim(w.d, w.n_terms)
     state_bytes = 2 * F * (w.dv + 1) * 4 * w.B * w.H   # read + write of S and z
+    # Same-shape read-modify-write ceiling: torch's in-place add over buffers
+    # of the state's size, round-robin over the same number of replicas and
+    # timed the same way; it reads and writes exactly the bytes a decode step
+    # moves, with no feature map or read-out.
+    del Ss, zs
+    bufs = [torch.empty(state_bytes // 8, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(R)]
+    for i in range(16):
+        bufs[i % R].add_(1.0)
+    ms_rmw = time_loop(lambda i: bufs[i % R].add_(1.0), w.steps, torch)
+    del bufs
     flops = 4 * F * (w.dv + 1) * w.B * w.H / 2            # 2F(dv+1) per head-step
     return {
         "workload": DECODE, "heads": w.B * w.H, "features": F, "steps_timed": w.steps,
@@ -285,6 +295,9 @@ def bench_decode(args, torch, tl, W):
         "state_GBps_hot": state_bytes / (ms_hot * 1e-3) / 1e9,
         "hbm_frac_cold": state_bytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "state_replicas_cold": R, "algorithmic_gflop_per_step": flops / 1e9,
+        "rmw_ceiling": {"us_per_step": ms_rmw * 1e3, "GBps": state_bytes / (ms_rmw * 1e-3) / 1e9,
+                        "hbm_frac": state_bytes / (ms_rmw * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "what": "torch in-place add over buffers of the state's size, same replicas and timing"},
         "kernel": "decode_kernel<16,64,3,fp32>",
     }
 

@@ -35,6 +35,32 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
     return reinterpret_cast<const float*>(p)[i];
 }
 
+// Sum of the read-out partials of a 256-thread block: thread tid holds the
+// numerator part `acc` of value columns 4 (tid % NQ) .. + 4 and a share
+// `dpart` of the denominator. The row groups inside a wave are summed with
+// lane exchanges, then the four waves' sums meet in LDS: afterwards red[c]
+// (c < NQ) holds the numerator of columns 4c .. 4c + 3 and dred[0] the
+// denominator, for every thread.
+template <int NQ>
+__device__ __forceinline__ void block_reduce(f32x4 acc, float dpart, f32x4* red, float* dred) {
+  static_assert(NQ == 4 || NQ == 16, "row groups tile a 64-lane wave");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int m = NQ; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], m);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) dpart += __shfl_xor(dpart, m);
+  if (lane < NQ) red[wv * NQ + lane] = acc;
+  if (lane == 0) dred[wv] = dpart;
+  __syncthreads();
+  if (tid < NQ) {
+    red[tid] = red[tid] + red[NQ + tid] + red[2 * NQ + tid] + red[3 * NQ + tid];
+    if (tid == 0) dred[0] = dred[0] + dred[1] + dred[2] + dred[3];
+  }
+  __syncthreads();
+}
+
 template <int D, int DV, int NT, bool BF16>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int F = feature_count(D, NT);
@@ -48,8 +74,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float sq[D], sk[D];
   __shared__ __attribute__((aligned(16))) float sv[DV];
   __shared__ float sfk[F], sfq[F];
-  __shared__ f32x4 red[256];
-  __shared__ float dred[256];
+  __shared__ f32x4 red[4 * NQ];
+  __shared__ float dred[4];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -140,16 +166,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       dpart += sfq[f] * zz;
     }
   }
-  red[tid] = acc;
-  dred[tid] = dpart;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) dred[tid] += dred[tid + s];
-    __syncthreads();
-  }
+  block_reduce<NQ>(acc, dpart, red, dred);
   if (tid < NQ) {
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < NG; ++g) num += red[g * NQ + tid];
+    const f32x4 num = red[tid];
     const float r = 1.f / dred[0];
     const size_t off = static_cast<size_t>(bh) * DV + 4 * tid;
     if (a.out_bf16) {
@@ -191,8 +210,8 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeArgs a) {
   __shared__ float sq[D], sk[D];
   __shared__ __attribute__((aligned(16))) float sv[DV];
   __shared__ float sfk[FB], sfq[FB];
-  __shared__ f32x4 red[256];
-  __shared__ float dred[256];
+  __shared__ f32x4 red[4 * NQ];
+  __shared__ float dred[4];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -290,16 +309,9 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeArgs a) {
       }
     }
   }
-  red[tid] = acc;
-  dred[tid] = dpart;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) dred[tid] += dred[tid + s];
-    __syncthreads();
-  }
+  block_reduce<NQ>(acc, dpart, red, dred);
   if (tid < NQ) {
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int gg = 0; gg < NG; ++gg) num += red[gg * NQ + tid];
+    const f32x4 num = red[tid];
     const float r = 1.f / dred[0];
     const size_t off = static_cast<size_t>(bh) * DV + 4 * tid;
     if (a.out_bf16) {
