@@ -515,6 +515,73 @@ def cpu_baseline(w, x, budget_s):
     return out
 
 
+def time_ext(torch, tl, W):
+    """Plain prefill against the extended entry point with a decay (0.999) and
+    with q/k normalisation plus scales (2, 2), on the shapes of the two order-2
+    bf16 workloads (the options run on the generic kernels). Prints one JSON
+    line per shape."""
+    for name in ("based_order2_prefill", "long_order2_prefill"):
+        w = W.WORKLOADS[name]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(3)
+        q, k = (torch.randn(w.B, w.H, w.N, w.d, device="cuda", generator=g).bfloat16() for _ in range(2))
+        v = torch.randn(w.B, w.H, w.N, w.dv, device="cuda", generator=g).bfloat16()
+        res = {"workload": name}
+        for label, kw in (("plain", {}), ("decay_0.999", {"gamma": 0.999}),
+                          ("qk_norm_scales_2", {"qk_norm": True, "q_scale": 2.0, "k_scale": 2.0})):
+            nb = tl.prefill_workspace_bytes(w.B, w.H, w.N, w.d, w.dv, w.n_terms, q.dtype, decayed=bool(kw))
+            ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+            call = lambda i: tl.prefill(q, k, v, w.n_terms, w.a, workspace=ws, **kw)
+            for i in range(3):
+                call(i)
+            res[label + "_ms"] = time_loop(call, 10, torch)
+        print(json.dumps(res), flush=True)
+
+
+def bench_order6(torch, tl):
+    """Order 6 (n_terms = 7, d = 16, dv = 64, F = 74,613; the generic kernels):
+    one prefill shape and one decode shape, random bf16 / fp32 inputs with
+    q and k rows at norm 2 (as in the order-4 workload). Algorithmic flops
+    and state bytes as for the other workloads."""
+    d, dv, n, a = 16, 64, 7, 4.0
+    F = feature_dim(d, n)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+
+    def rows(shape, dt):
+        x = torch.randn(*shape, device="cuda", generator=g)
+        return (2.0 * x / x.norm(dim=-1, keepdim=True)).to(dt)
+    B, H, N = 2, 8, 2048
+    q, k = rows((B, H, N, d), torch.bfloat16), rows((B, H, N, d), torch.bfloat16)
+    v = torch.randn(B, H, N, dv, device="cuda", generator=g).bfloat16()
+    ws = torch.empty(max(tl.prefill_workspace_bytes(B, H, N, d, dv, n, q.dtype), 1), dtype=torch.uint8,
+                     device="cuda")
+    call = lambda i: tl.prefill(q, k, v, n, a, workspace=ws)
+    for i in range(2):
+        call(i)
+    ms = time_loop(call, 5, torch)
+    flops = B * H * N * (4 * F * (dv + 1) + (CHUNK + 1) * (d + dv + 1))
+    out = {"prefill": {"B": B, "H": H, "N": N, "dtype": "bf16", "ms_per_call": ms,
+                       "tokens_per_s": B * N / (ms * 1e-3), "mfma_tflops": flops / (ms * 1e-3) / 1e12,
+                       "mfma_frac": flops / (ms * 1e-3) / 1e12 / BF16_DENSE_TFLOPS}}
+    del q, k, v, ws
+    Bd, Hd = 8, 16
+    S = torch.randn(Bd, Hd, F, dv, device="cuda", generator=g) * 0.01
+    z = torch.rand(Bd, Hd, F, device="cuda", generator=g) + 1.0
+    qd, kd = rows((8, Bd, Hd, d), torch.float32), rows((8, Bd, Hd, d), torch.float32)
+    vd = torch.randn(8, Bd, Hd, dv, device="cuda", generator=g)
+    step = lambda i: tl.decode(qd[i % 8], kd[i % 8], vd[i % 8], S, z, n, a)
+    for i in range(2):
+        step(i)
+    msd = time_loop(step, 16, torch)
+    nbytes = 2 * F * (dv + 1) * 4 * Bd * Hd
+    out["decode"] = {"heads": Bd * Hd, "us_per_step": msd * 1e3, "state_bytes_per_step": nbytes,
+                     "state_GBps": nbytes / (msd * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (msd * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    out["features"] = F
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -534,6 +601,9 @@ def main():
                     help="time one prefill call of each named workload, then exit")
     ap.add_argument("--sweep", action="store_true",
                     help="growth of prefill time with N and of decode time with the context, then exit")
+    ap.add_argument("--ext", action="store_true",
+                    help="time the extended entry point (decay, q/k preprocessing) against the plain one on the "
+                         "two order-2 workload shapes, then exit")
     ap.add_argument("--pmc-summary", nargs=5,
                     metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise rocprofv3 --pmc runs into the workload's stored traffic record and exit")
@@ -555,6 +625,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         sweep(args, torch, tl)
+        return
+    if args.ext:
+        time_ext(torch, tl, W)
         return
     if args.time:
         time_workloads(args.time, torch, tl, W)
@@ -616,6 +689,8 @@ def main():
             r = bench_prefill(name, st, args.warmup, torch, tl, W)
             out[name] = prefill_block(name, *r[:6], st)
             del r
+        log("order 6: prefill and decode")
+        out["order6"] = bench_order6(torch, tl)
     if not args.no_decode:
         out["decode"] = bench_decode(args, torch, tl, W)
     if not args.no_native:

@@ -35,13 +35,13 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
     return reinterpret_cast<const float*>(p)[i];
 }
 
-// Sum of the read-out partials of a 256-thread block: thread tid holds the
+// Sum of the read-out partials of a block of NWV waves: thread tid holds the
 // numerator part `acc` of value columns 4 (tid % NQ) .. + 4 and a share
 // `dpart` of the denominator. The row groups inside a wave are summed with
-// lane exchanges, then the four waves' sums meet in LDS: afterwards red[c]
+// lane exchanges, then the waves' sums meet in LDS: afterwards red[c]
 // (c < NQ) holds the numerator of columns 4c .. 4c + 3 and dred[0] the
 // denominator, for every thread.
-template <int NQ>
+template <int NQ, int NWV = 4>
 __device__ __forceinline__ void block_reduce(f32x4 acc, float dpart, f32x4* red, float* dred) {
   static_assert(NQ == 4 || NQ == 16, "row groups tile a 64-lane wave");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -55,8 +55,16 @@ __device__ __forceinline__ void block_reduce(f32x4 acc, float dpart, f32x4* red,
   if (lane == 0) dred[wv] = dpart;
   __syncthreads();
   if (tid < NQ) {
-    red[tid] = red[tid] + red[NQ + tid] + red[2 * NQ + tid] + red[3 * NQ + tid];
-    if (tid == 0) dred[0] = dred[0] + dred[1] + dred[2] + dred[3];
+    f32x4 t = red[tid];
+#pragma unroll
+    for (int v = 1; v < NWV; ++v) t += red[v * NQ + tid];
+    red[tid] = t;
+    if (tid == 0) {
+      float dd = dred[0];
+#pragma unroll
+      for (int v = 1; v < NWV; ++v) dd += dred[v];
+      dred[0] = dd;
+    }
   }
   __syncthreads();
 }
@@ -197,21 +205,22 @@ __device__ __forceinline__ float inv_factorial(int m) {
 // decode_kernel (read, update, write back, fold into the read-out). The
 // first rows of a block are requested before its features are generated.
 template <int D, int DV, int NT, bool BF16>
-__global__ __launch_bounds__(256) void decode_wide_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void decode_wide_kernel(DecodeArgs a) {
+  constexpr int NT_ = 1024;                // threads: a 19 MB state per head needs many loads in flight
   constexpr int F = feature_count(D, NT);
-  constexpr int FB = 2048;                // state rows per block
-  constexpr int RUN = FB / 256;           // features generated per thread and block
+  constexpr int FB = 4096;                // state rows per block
+  constexpr int RUN = FB / NT_;           // features generated per thread and block
   constexpr int NQ = DV / 4;              // float4 columns per state row
-  constexpr int NG = 256 / NQ;            // row groups
+  constexpr int NG = NT_ / NQ;            // row groups
   constexpr int RPB = FB / NG;            // rows per row group and block
   constexpr int BATCH = 8;                // rows in flight per thread
-  static_assert(RPB % BATCH == 0 && FB % 256 == 0, "block shape");
+  static_assert(RPB % BATCH == 0 && FB % NT_ == 0, "block shape");
 
   __shared__ float sq[D], sk[D];
   __shared__ __attribute__((aligned(16))) float sv[DV];
   __shared__ float sfk[FB], sfq[FB];
-  __shared__ f32x4 red[4 * NQ];
-  __shared__ float dred[4];
+  __shared__ f32x4 red[(NT_ / 64) * NQ];
+  __shared__ float dred[NT_ / 64];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -293,15 +302,15 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeArgs a) {
         }
       }
     }
-    float zv[FB / 256];
+    float zv[FB / NT_];
 #pragma unroll
-    for (int j = 0; j < FB / 256; ++j) {
-      const int f = f0 + tid + 256 * j;
+    for (int j = 0; j < FB / NT_; ++j) {
+      const int f = f0 + tid + NT_ * j;
       zv[j] = f < F ? __builtin_nontemporal_load(zh + f) : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < FB / 256; ++j) {
-      const int fl = tid + 256 * j;
+    for (int j = 0; j < FB / NT_; ++j) {
+      const int fl = tid + NT_ * j;
       if (f0 + fl < F) {
         const float zz = zv[j] * g + sfk[fl];
         __builtin_nontemporal_store(zz, zh + f0 + fl);
@@ -309,7 +318,7 @@ __global__ __launch_bounds__(256) void decode_wide_kernel(DecodeArgs a) {
       }
     }
   }
-  block_reduce<NQ>(acc, dpart, red, dred);
+  block_reduce<NQ, NT_ / 64>(acc, dpart, red, dred);
   if (tid < NQ) {
     const f32x4 num = red[tid];
     const float r = 1.f / dred[0];
@@ -405,9 +414,9 @@ hipError_t decode_launch(int d, int dv, int n_terms, bool bf16, const DecodeArgs
   // bases too wide for the LDS-resident features
   if (d == 16 && dv == 64 && n_terms == 7) {
     if (bf16)
-      hipLaunchKernelGGL((decode_wide_kernel<16, 64, 7, true>), dim3(a.BH), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_wide_kernel<16, 64, 7, true>), dim3(a.BH), dim3(1024), 0, stream, a);
     else
-      hipLaunchKernelGGL((decode_wide_kernel<16, 64, 7, false>), dim3(a.BH), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((decode_wide_kernel<16, 64, 7, false>), dim3(a.BH), dim3(1024), 0, stream, a);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
