@@ -320,24 +320,24 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 // accumulator rows 16 ks + 4 lh + {0..3} and 16 ks + 8 + 4 lh + {0..3}
 __device__ __forceinline__ constexpr int fpos(int s) { return s < 4 ? s : s + 4; }
 
-enum { SEGSUM = 0, MAIN = 1 };
-
-template <int MODE, bool OBF>
+// Main launch: every segment from its inclusive prefix; outputs and, for the
+// last segment, the final state.
+template <bool OBF>
 __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[LDS];
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lc = l & 31, lh = l >> 5;
 
-  const int PL = MODE == MAIN ? a.P : a.P - 1;
+  const int PL = a.P;
   const int unit = blockIdx.x;
   if (unit >= a.BH * 2 * PL) return;
   const int bhh = unit / PL;  // head * 2 + value half
   const int p = unit - bhh * PL;
   const int bh = bhh >> 1, hv = bhh & 1;
-  const bool want_out = MODE == MAIN && a.o != nullptr;
-  const bool want_state = MODE == MAIN && a.S != nullptr && p == a.P - 1;
-  if (MODE == MAIN && !want_out && !want_state) return;
+  const bool want_out = a.o != nullptr;
+  const bool want_state = a.S != nullptr && p == a.P - 1;
+  if (!want_out && !want_state) return;
   const int N = a.N;
   const int t0 = p * a.L;
   const int t1 = min(N, t0 + a.L);
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   uint4 ra, rvv;  // one chunk ahead: the chunk's compute covers the load latency
   auto stage = [&](int c, int b) __attribute__((always_inline)) {
     const bf16x8 x = __builtin_bit_cast(bf16x8, ra);
-    if (MODE == MAIN && is_q) {
+    if (is_q) {
       *reinterpret_cast<bf16x8*>(qr(b) + irow * QRP + 8 * ic8) = x;
       f32x4 lo, hi;
 #pragma unroll
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
       *reinterpret_cast<f32x4*>(row + D) = lo;
       *reinterpret_cast<f32x4*>(row + D + 4) = hi;
     } else if (!is_q) {
-      if (MODE == MAIN) *reinterpret_cast<bf16x8*>(kr(b) + irow * KRP + 8 * ic8) = x;
+      *reinterpret_cast<bf16x8*>(kr(b) + irow * KRP + 8 * ic8) = x;
       const f16x8 h = b2h(x);
       _Float16* t = kt(b);
 #pragma unroll
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   auto unit_at = [&](int q) __attribute__((always_inline)) {
     return segp + (static_cast<size_t>(bhh) * a.P + q) * UNIT_F4;
   };
-  const float z0base = MODE == MAIN ? unit_at(p)[Z0_F4].x : 0.f;
+  const float z0base = unit_at(p)[Z0_F4].x;
 
   // sum the partials of chunk i, normalise, store rows
   auto finalize = [&](int i) __attribute__((always_inline)) {
@@ -667,7 +667,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     float z1r = 0.f;  // wave W_AUX: z1 of coordinate l
 
     // initial state: unit p
-    if (MODE == MAIN) {
+    {
       const float4* src = unit_at(p) + l;
 #pragma unroll
       for (int i = 0; i < NSW; ++i)
@@ -698,12 +698,10 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
 
     // results
     float4* dstu = nullptr;
-    if (MODE == SEGSUM) {
-      dstu = reinterpret_cast<float4*>(a.seg) + (static_cast<size_t>(bhh) * a.P + p + 1) * UNIT_F4;
-    } else if (want_state && a.defer_state) {
+    if (want_state && a.defer_state) {
       dstu = reinterpret_cast<float4*>(a.fin) + static_cast<size_t>(bhh) * UNIT_F4;
     }
-    const float count = (MODE == MAIN ? z0base : 0.f) + static_cast<float>(t1 - t0);
+    const float count = z0base + static_cast<float>(t1 - t0);
     if (dstu != nullptr) {
 #pragma unroll
       for (int sl = 0; sl < NSW; ++sl)
@@ -1144,9 +1142,9 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.o == nullptr || a.out_bf16)
-    hipLaunchKernelGGL((w2_kernel<MAIN, true>), dim3(a.BH * 2 * a.P), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((w2_kernel<true>), dim3(a.BH * 2 * a.P), dim3(NTHR), 0, stream, a);
   else
-    hipLaunchKernelGGL((w2_kernel<MAIN, false>), dim3(a.BH * 2 * a.P), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((w2_kernel<false>), dim3(a.BH * 2 * a.P), dim3(NTHR), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.defer_state && a.S != nullptr) {
     hipLaunchKernelGGL(w2_state_store, dim3(a.BH * 2 * (NSLOT + 1)), dim3(64), 0, stream,
