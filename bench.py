@@ -582,6 +582,25 @@ def bench_order6(torch, tl):
     return out
 
 
+def time_fmap(torch, tl):
+    """The standalone feature map: rows of bf16 inputs -> [rows, F] fp32. It
+    is bound by the HBM write of the output (4F bytes per row; the input adds
+    2d). Prints one JSON line per (d, n_terms)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    for d, n, rows in ((16, 3, 1 << 20), (16, 5, 1 << 16), (64, 3, 1 << 17), (16, 7, 1 << 12)):
+        x = torch.randn(rows, d, device="cuda", generator=g).bfloat16()
+        F = feature_dim(d, n)
+        call = lambda i: tl.feature_map(x, n, a=math.sqrt(d))
+        for i in range(2):
+            call(i)
+        ms = time_loop(call, 10, torch)
+        nbytes = rows * (4 * F + 2 * d)
+        print(json.dumps({"d": d, "n_terms": n, "features": F, "rows": rows, "ms": ms,
+                          "GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}),
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -601,6 +620,8 @@ def main():
                     help="time one prefill call of each named workload, then exit")
     ap.add_argument("--sweep", action="store_true",
                     help="growth of prefill time with N and of decode time with the context, then exit")
+    ap.add_argument("--fmap", action="store_true",
+                    help="time the standalone feature map (taylor_feature_map) on a few widths, then exit")
     ap.add_argument("--ext", action="store_true",
                     help="time the extended entry point (decay, q/k preprocessing) against the plain one on the "
                          "two order-2 workload shapes, then exit")
@@ -628,6 +649,9 @@ def main():
         return
     if args.ext:
         time_ext(torch, tl, W)
+        return
+    if args.fmap:
+        time_fmap(torch, tl)
         return
     if args.time:
         time_workloads(args.time, torch, tl, W)

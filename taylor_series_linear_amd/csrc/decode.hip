@@ -334,48 +334,51 @@ __global__ __launch_bounds__(1024) void decode_wide_kernel(DecodeArgs a) {
   }
 }
 
-// Feature map of a basis without a compile-time table: each thread writes a
-// run of RUN consecutive features of one row, decoding the first and
-// stepping through the rest.
-template <int D, int NT, bool BF16>
-__global__ __launch_bounds__(256) void feature_map_wide_kernel(const void* x, int64_t rows, float* phi,
-                                                               OrderScale sc) {
-  constexpr int F = feature_count(D, NT);
-  constexpr int RUN = 16;
-  constexpr int RPR = (F + RUN - 1) / RUN;  // runs per row
-  const int64_t total = rows * RPR;
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; u < total;
-       u += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t r = u / RPR;
-    const int f0 = static_cast<int>(u - r * RPR) * RUN;
-    RankedFeature e = rank_decode(D, NT, f0);
-    for (int j = 0; j < RUN && f0 + j < F; ++j) {
-      float v = e.w * sc.s[e.m];
-#pragma unroll
-      for (int t = 0; t < kMaxOrderRank; ++t)
-        if (t < e.m) v *= load_in<BF16>(x, static_cast<size_t>(r) * D + e.idx[t]);
-      phi[r * F + f0 + j] = v;
-      rank_next(D, e);
-    }
-  }
-}
-
-// phi[row, f] = w_f * prod_j x[row, i_j] * scale[m_f]
+// Feature map, phi[row, f] = w_f * scale[m_f] * prod_j x[row, i_j]. A
+// workgroup covers a block of FM_ROWS rows and FM_FPT * 256 consecutive
+// features: every thread decodes its first feature once and steps through
+// the rest (no per-element index arithmetic or table lookup), the block's
+// input rows are staged in LDS, and each row's outputs are written by
+// consecutive threads, so the stores of a wave cover one contiguous stretch
+// of the output row. The kernel is bound by the HBM write of phi.
+constexpr int FM_ROWS = 64;
+constexpr int FM_FPT = 4;  // features per thread
 template <int D, int NT, bool BF16>
 __global__ __launch_bounds__(256) void feature_map_kernel(const void* x, int64_t rows, float* phi,
                                                           OrderScale sc) {
   constexpr int F = feature_count(D, NT);
-  const auto& tab = g_dtab<D, NT>;
-  const int64_t total = rows * F;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
-       e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t r = e / F;
-    const int f = static_cast<int>(e - r * F);
-    const PackedFeature pf = tab.e[f];
-    const int m = static_cast<int>(pf.m);
-    float v = pf.w * sc.s[m];
-    for (int j = 0; j < m; ++j) v *= load_in<BF16>(x, static_cast<size_t>(r) * D + ((pf.idx >> (8 * j)) & 255));
-    phi[e] = v;
+  __shared__ float xs[FM_ROWS * D];
+  const int tid = threadIdx.x;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * FM_ROWS;
+  const int nr = static_cast<int>(rows - r0 < FM_ROWS ? rows - r0 : FM_ROWS);
+  for (int i = tid; i < nr * D; i += 256) xs[i] = load_in<BF16>(x, static_cast<size_t>(r0) * D + i);
+  __syncthreads();
+  const int f0 = (static_cast<int>(blockIdx.y) * 256 + tid) * FM_FPT;
+  if (f0 >= F) return;
+  // this thread's features: coefficient and indices, in registers
+  float cf[FM_FPT];
+  int ix[FM_FPT][kMaxOrderRank];
+  int mm[FM_FPT];
+  RankedFeature e = rank_decode(D, NT, f0);
+#pragma unroll
+  for (int j = 0; j < FM_FPT; ++j) {
+    cf[j] = f0 + j < F ? e.w * sc.s[e.m] : 0.f;
+    mm[j] = e.m;
+#pragma unroll
+    for (int u = 0; u < kMaxOrderRank; ++u) ix[j][u] = e.idx[u];
+    if (j + 1 < FM_FPT) rank_next(D, e);
+  }
+  for (int r = 0; r < nr; ++r) {
+    const float* xr = xs + r * D;
+    float* dst = phi + (r0 + r) * F + f0;
+#pragma unroll
+    for (int j = 0; j < FM_FPT; ++j) {
+      float v = cf[j];
+#pragma unroll
+      for (int u = 0; u < kMaxOrderRank; ++u)
+        if (u < mm[j]) v *= xr[ix[j][u]];
+      if (f0 + j < F) dst[j] = v;
+    }
   }
 }
 
@@ -424,31 +427,20 @@ hipError_t decode_launch(int d, int dv, int n_terms, bool bf16, const DecodeArgs
 
 hipError_t feature_map_launch(int d, int n_terms, bool bf16, const void* x, int64_t rows,
                               float* phi, const OrderScale& sc, hipStream_t stream) {
-  const int64_t total = rows * feature_count(d, n_terms);
-  const int64_t want = (total + 255) / 256;
-  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
-#define X(D, NT)                                                                                  \
-  if (d == D && n_terms == NT) {                                                                  \
-    if (bf16)                                                                                     \
-      hipLaunchKernelGGL((feature_map_kernel<D, NT, true>), dim3(blocks), dim3(256), 0, stream, x, \
-                         rows, phi, sc);                                                          \
-    else                                                                                          \
-      hipLaunchKernelGGL((feature_map_kernel<D, NT, false>), dim3(blocks), dim3(256), 0, stream,  \
-                         x, rows, phi, sc);                                                       \
-    return hipGetLastError();                                                                     \
+  if (rows <= 0) return hipSuccess;
+  const int64_t rb = (rows + FM_ROWS - 1) / FM_ROWS;
+  if (rb > 0x7fffffff) return hipErrorInvalidValue;
+#define X(D, NT)                                                                                       \
+  if (d == D && n_terms == NT) {                                                                       \
+    const dim3 grid(static_cast<unsigned>(rb), (feature_count(D, NT) + 256 * FM_FPT - 1) / (256 * FM_FPT)); \
+    if (bf16)                                                                                          \
+      hipLaunchKernelGGL((feature_map_kernel<D, NT, true>), grid, dim3(256), 0, stream, x, rows, phi, sc); \
+    else                                                                                               \
+      hipLaunchKernelGGL((feature_map_kernel<D, NT, false>), grid, dim3(256), 0, stream, x, rows, phi, sc); \
+    return hipGetLastError();                                                                          \
   }
-  X(16, 1) X(16, 3) X(16, 5) X(32, 1) X(32, 3) X(64, 1) X(64, 3)
+  X(16, 1) X(16, 3) X(16, 5) X(16, 7) X(32, 1) X(32, 3) X(64, 1) X(64, 3)
 #undef X
-  if (d == 16 && n_terms == 7) {
-    constexpr int F = feature_count(16, 7);
-    const int64_t runs = rows * ((F + 15) / 16);
-    const unsigned wb = static_cast<unsigned>((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
-    if (bf16)
-      hipLaunchKernelGGL((feature_map_wide_kernel<16, 7, true>), dim3(wb), dim3(256), 0, stream, x, rows, phi, sc);
-    else
-      hipLaunchKernelGGL((feature_map_wide_kernel<16, 7, false>), dim3(wb), dim3(256), 0, stream, x, rows, phi, sc);
-    return hipGetLastError();
-  }
   return hipErrorInvalidValue;
 }
 
