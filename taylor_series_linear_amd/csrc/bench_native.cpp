@@ -11,8 +11,11 @@
 //    used round-robin (325 MB, more than the last-level cache), "hot" on one.
 //  * Based-style order-2 prefill: B = 4, H = 16, N = 4096, d = 16, dv = 64,
 //    bf16 in and out, a = 4; 200 calls over 4 input replicas.
-// Each phase runs 64 untimed calls first; times come from HIP events around
-// the timed calls on the null stream. Prints one JSON line.
+//  * long-context order-2 prefill: B = 1, H = 8, N = 65536, d = 64, dv = 64,
+//    bf16 in and out, a = 8; 20 calls over 2 input replicas (3 untimed).
+// The decode and the d = 16 prefill run 64 untimed calls first; times come
+// from HIP events around the timed calls on the null stream. Prints one JSON
+// line.
 //
 // Usage: bench_native [decode_steps] [prefill_calls]
 #include <hip/hip_runtime.h>
@@ -170,15 +173,46 @@ int main(int argc, char** argv) {
   const double pf_bytes = static_cast<double>(PB) * PH * PN * ((2.0 * d + dv) * 2 + dv * 2);
   hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
 
+  // ---- long-context order-2 prefill (d = 64) -------------------------------
+  const int LB = 1, LH = 8, LN = 65536, LD = 64, LR = 2, LC = calls < 20 ? calls : 20;
+  const float la = 8.f;
+  const size_t lqk = static_cast<size_t>(LB) * LH * LN * LD;
+  const auto lq = to_bf16(normals(lqk, 1005)), lk = to_bf16(normals(lqk, 1015)), lv = to_bf16(normals(lqk, 1025));
+  std::vector<void*> q2(LR), k2(LR), v2(LR), o2(LR);
+  for (int r = 0; r < LR; ++r) {
+    q2[r] = upload(lq);
+    k2[r] = upload(lk);
+    v2[r] = upload(lv);
+    o2[r] = alloc(lqk * 2);
+  }
+  const size_t lwsb = taylor_attn_prefill_workspace(LB, LH, LN, LD, dv, n, TAYLOR_BF16);
+  void* lws = alloc(lwsb);
+  auto lcall = [&](int i) {
+    const int r = i % LR;
+    const taylor_status st = taylor_attn_prefill(q2[r], k2[r], v2[r], TAYLOR_BF16, LB, LH, LN, LD, dv, n, la,
+                                                 nullptr, nullptr, o2[r], TAYLOR_BF16, nullptr, nullptr, lws, lwsb,
+                                                 nullptr);
+    if (st != TAYLOR_OK) tl_check(st, "long prefill");
+  };
+  for (int i = 0; i < 3; ++i) lcall(i);
+  const double ms_long = time_calls(0, LC, lcall);
+  const int64_t LF = taylor_feature_dim(LD, n);
+  const double long_flops = static_cast<double>(LB) * LH * LN * (4.0 * LF * (dv + 1) + 33.0 * (LD + dv + 1));
+  hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+
   std::printf(
       "{\"hip_runtime_version\": %d, "
       "\"decode\": {\"heads\": %zu, \"features\": %lld, \"steps_timed\": %d, \"state_replicas_cold\": %d, "
       "\"us_per_step_cold\": %.3f, \"us_per_step_hot\": %.3f, \"state_GBps_cold\": %.1f, "
       "\"hbm_frac_cold\": %.4f}, "
       "\"prefill\": {\"B\": %d, \"H\": %d, \"N\": %d, \"calls_timed\": %d, \"input_replicas\": %d, "
-      "\"us_per_call\": %.3f, \"tokens_per_s\": %.4e, \"algorithmic_GBps\": %.1f, \"hbm_frac\": %.4f}}\n",
+      "\"us_per_call\": %.3f, \"tokens_per_s\": %.4e, \"algorithmic_GBps\": %.1f, \"hbm_frac\": %.4f}, "
+      "\"long_prefill\": {\"B\": %d, \"H\": %d, \"N\": %d, \"d\": %d, \"calls_timed\": %d, \"input_replicas\": %d, "
+      "\"ms_per_call\": %.4f, \"tokens_per_s\": %.4e, \"algorithmic_TFLOPs\": %.1f, \"mfma_frac\": %.4f}}\n",
       runtime, heads, static_cast<long long>(F), steps, R, ms_cold * 1e3, ms_hot * 1e3,
       state_bytes / (ms_cold * 1e-3) / 1e9, state_bytes / (ms_cold * 1e-3) / 8e12, PB, PH, PN, calls, PR, ms_pf * 1e3,
-      PB * PN / (ms_pf * 1e-3), pf_bytes / (ms_pf * 1e-3) / 1e9, pf_bytes / (ms_pf * 1e-3) / 8e12);
+      PB * PN / (ms_pf * 1e-3), pf_bytes / (ms_pf * 1e-3) / 1e9, pf_bytes / (ms_pf * 1e-3) / 8e12, LB, LH, LN, LD,
+      LC, LR, ms_long, LB * LN / (ms_long * 1e-3), long_flops / (ms_long * 1e-3) / 1e12,
+      long_flops / (ms_long * 1e-3) / 1e12 / 2500.0);
   return 0;
 }
