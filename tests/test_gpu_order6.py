@@ -149,3 +149,27 @@ def test_order6_decode_from_oracle_state():
     torch.cuda.synchronize()
     ref = T.direct(x["q64"], x["k64"], x["v64"], NT, A)[:, :, N]
     check_parity(to_f64(od)[:, :, None], ref[:, :, None], "f32", say=say)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_order6_ext_decay_and_decode(dtype):
+    # the extended entry points at order 6: q/k rows normalised and scaled by
+    # 2 (the order-4 workload's recipe), a decay 0.99, several segments, then
+    # two decode steps with the same options; against the oracle on the
+    # preprocessed rows
+    B, H, N, steps, g = 1, 2, 1200, 2, 0.99
+    x = W.make_qkv(B, H, N + steps, D, DV, dtype, 617, "normal")
+    q, k, v = _dev(x, dtype)
+    opts = dict(qk_norm=True, q_scale=2.0, k_scale=2.0, gamma=g)
+    say("order-6 ext + decay + decode", dtype)
+    o, S, z = tl.prefill(q[:, :, :N].contiguous(), k[:, :, :N].contiguous(), v[:, :, :N].contiguous(), NT, A,
+                         out_dtype=torch.float32, return_state=True, **opts)
+    outs = [tl.decode(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(), S, z, NT, A,
+                      out_dtype=torch.float32, **opts) for t in range(N, N + steps)]
+    torch.cuda.synchronize()
+    qp = T.preprocess(x["q64"], True, 2.0)
+    kp = T.preprocess(x["k64"], True, 2.0)
+    ref = T.direct(qp, kp, x["v64"], NT, A, gamma=g)
+    check_parity(to_f64(o), ref[:, :, :N], dtype, say=say)
+    got = np.stack([to_f64(t) for t in outs], axis=2)
+    check_parity(got, ref[:, :, N:], dtype, say=say, what="decode: ")
