@@ -628,7 +628,9 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
   auto unit_at = [&](int q) __attribute__((always_inline)) {
     return segp + (static_cast<size_t>(bhh) * a.P + q) * UNIT_F4;
   };
-  const float z0base = unit_at(p)[Z0_F4].x;
+  // unit 0 is written only when there is an initial state (zero otherwise)
+  const bool from_unit = p > 0 || a.S0 != nullptr;
+  const float z0base = from_unit ? unit_at(p)[Z0_F4].x : 0.f;
 
   // sum the partials of chunk i, normalise, store rows
   auto finalize = [&](int i) __attribute__((always_inline)) {
@@ -667,7 +669,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     float z1r = 0.f;  // wave W_AUX: z1 of coordinate l
 
     // initial state: unit p
-    {
+    if (from_unit) {
       const float4* src = unit_at(p) + l;
 #pragma unroll
       for (int i = 0; i < NSW; ++i)
@@ -1002,9 +1004,10 @@ __global__ __launch_bounds__(NTHR, 1) void w2_segsum_fs(PrefillArgs a) {
     per_wave(std::integral_constant<int, 1>{});
 }
 
-// Unit 0 of each (head, half): S0/z0 in the internal layout (zeros without
-// an initial state). One workgroup of 64 threads per (head, half, slot), plus
-// one per (head, half) for z1 and z0.
+// Unit 0 of each (head, half): S0/z0 in the internal layout (launched only
+// with an initial state; without one the scan and the main launch take unit
+// 0 as zero and never read it). One workgroup of 64 threads per (head, half,
+// slot), plus one per (head, half) for z1 and z0.
 __global__ __launch_bounds__(64) void w2_s0_unit(const float* S0, const float* z0, float4* seg, int P) {
   const int u = blockIdx.x / (NSLOT + 1), s = blockIdx.x % (NSLOT + 1);
   const int bh = u >> 1, hv = u & 1;
@@ -1038,12 +1041,12 @@ __global__ __launch_bounds__(64) void w2_s0_unit(const float* S0, const float* z
 }
 
 // Inclusive prefix over the segments of each (head, half), in place.
-__global__ __launch_bounds__(256) void w2_scan(float4* seg, int BHH, int PS) {
+__global__ __launch_bounds__(256) void w2_scan(float4* seg, int BHH, int PS, int has_s0) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (e >= static_cast<int64_t>(BHH) * UNIT_F4) return;
   const int64_t u = e / UNIT_F4, pos = e - u * UNIT_F4;
   float4* base = seg + u * PS * static_cast<int64_t>(UNIT_F4) + pos;
-  float4 acc = base[0];
+  float4 acc = has_s0 ? base[0] : float4{0.f, 0.f, 0.f, 0.f};  // unit 0: S0 (zero without one)
   constexpr int B8 = 8;
   for (int p0 = 1; p0 < PS; p0 += B8) {
     float4 x[B8];
@@ -1131,14 +1134,16 @@ bool plan(int BH, int N, PrefillPlan* pl) {
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   hipError_t e;
   float4* seg = reinterpret_cast<float4*>(a.seg);
-  hipLaunchKernelGGL(w2_s0_unit, dim3(a.BH * 2 * (NSLOT + 1)), dim3(64), 0, stream, a.S0, a.z0, seg, a.P);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.S0 != nullptr) {
+    hipLaunchKernelGGL(w2_s0_unit, dim3(a.BH * 2 * (NSLOT + 1)), dim3(64), 0, stream, a.S0, a.z0, seg, a.P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.P > 1) {
     hipLaunchKernelGGL(w2_segsum_fs, dim3(a.BH * 2 * (a.P - 1)), dim3(NTHR), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = static_cast<int64_t>(a.BH) * 2 * UNIT_F4;
     hipLaunchKernelGGL(w2_scan, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, seg, a.BH * 2,
-                       a.P);
+                       a.P, a.S0 != nullptr ? 1 : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.o == nullptr || a.out_bf16)
