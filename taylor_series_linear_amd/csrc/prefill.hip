@@ -67,6 +67,7 @@ __device__ __forceinline__ float taylor_poly(float t) {
 
 template <int D_, int DV_, int NT_, bool BF16_, int FS_, int C_, bool UNROLL_>
 struct PCfg {
+  static constexpr bool ZS_() { return !UNROLL_ && DV_ == 64; }
   static constexpr int D = D_, DV = DV_, NT = NT_, FS = FS_, C = C_;
   static constexpr bool BF16 = BF16_, UNROLL = UNROLL_;
   using M = Mma<BF16>;
@@ -74,11 +75,32 @@ struct PCfg {
   static constexpr int ES = sizeof(E);
   static constexpr int F = feature_count(D, NT);
   static constexpr int G = (F + FS - 1) / FS;
-  static constexpr int NW = DV / 16 + 1;
+  // Denominator state z (the state of the ones column of [V, 1]). With the
+  // table-driven generator at dv = 64 ("split z") eight waves, two per SIMD,
+  // hold the state: wave w the value tiles 2 (w % 2) and 2 (w % 2) + 1 of
+  // feature group w / 2 (a quarter of the slice), and z for a share of that
+  // group's read-out k-steps, so that every phi fragment read from LDS feeds
+  // two or three MFMAs. Otherwise one wave per value tile holds all of the
+  // slice's features and a last wave holds z as a sixteen-column tile.
+  static constexpr bool ZS = ZS_();
+  static constexpr int NDT = ZS ? 2 : 1;  // value tiles per wave
+  static constexpr int NFG = ZS ? 4 : 1;  // feature groups
+  static constexpr int NW = ZS ? (DV / 16 / NDT) * NFG : DV / 16 + 1;
   static constexpr int NTHR = NW * 64;
-  static constexpr int DVP = NW * 16;
-  static constexpr int FT = FS / 16;   // 16-feature tiles per slice
-  static constexpr int KSF = FS / 32;  // read-out k-steps
+  static constexpr int DVP = (DV / 16 + 1) * 16;  // V^T rows: values, the ones row, zero padding
+  static constexpr int FT = FS / 16;    // 16-feature tiles per slice
+  static constexpr int KSF = FS / 32;   // read-out k-steps
+  static constexpr int FTG = FT / NFG;  // feature tiles per group
+  static constexpr int KSG = KSF / NFG; // read-out k-steps per group
+  // split z: in each feature group the wave of dv pair 0 holds z for the
+  // group's k-steps [0, KZ0), the wave of dv pair 1 for [KZ0, KSG)
+  static constexpr int KZ0 = KSG / 2;
+  static constexpr int ZT = ZS ? 2 * (KSG - KZ0) : 0;  // z tiles per wave (at most)
+  // per-(unit, slice) state in the accumulator layout: NW waves x (NDT FTG
+  // value tiles + ZT z tiles) x 64 lanes of float4
+  static constexpr int TPW = NDT * FTG + ZT;
+  static constexpr size_t SLICE_F4 = static_cast<size_t>(NW) * TPW * 64;
+  static constexpr int NDEN = 1;  // denominator columns of a partial-output row
   static constexpr int QT = C / 16;    // query tiles per chunk
   static constexpr int KSC = C / 32;   // key k-steps per chunk
   static constexpr int PADE = 16 / ES; // 16 bytes of padding, in elements
@@ -113,14 +135,23 @@ struct PCfg {
   static constexpr float KS = KH ? 0.5f : 1.f;
   static constexpr int KES = KH ? 2 : ES;
   static constexpr int TPK = KH ? C + 8 : C + 4;
-  static constexpr int OFF_TQ = OFF_DEN + C * 4;
+  // (split z: the denominator shares of all waves, [NW][C])
+  static constexpr int OFF_TQ = OFF_DEN + (ZS_() ? NW : 1) * C * 4;
   static constexpr int OFF_TK = OFF_TQ + TE * TP * 4;
-  static constexpr int LDS = OFF_TK + TE * TPK * KES;
+  static constexpr int TAB_END = OFF_TK + TE * TPK * KES;
+  // split z: the read-out partials of feature groups 1 .. NFG-1 ([NFG-1][C]
+  // [DV], f32x4 per lane and tile) reuse the factor tables, which are dead
+  // from the feature generation to the next chunk's staging
+  static constexpr int OFF_RED = OFF_TQ;
+  static constexpr int RED_END = OFF_RED + (ZS_() ? (NFG - 1) * C * DV * 4 : 0);
+  static constexpr int LDS = TAB_END > RED_END ? TAB_END : RED_END;
   static_assert(NT <= 7, "features are products of at most three table entries (order 6)");
   static_assert(!TRIPLE || (PAIRS && !UNROLL), "orders 5 and 6 use the table-driven generator with pairs");
   static_assert(FS % 32 == 0 && C % 32 == 0 && DV % 16 == 0, "tile multiples");
   static_assert(D % 16 == 0, "head dim multiple of 16");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(DV + NDEN <= PPITCH, "partial-output row holds the values and the denominator columns");
+  static_assert(!ZS || (FS % (32 * NFG) == 0 && DV == 16 * NDT * (NW / NFG)), "split z: whole k-steps per group");
   // score tiles (kt, qt) needed per chunk: key tiles up to the end of the
   // 32-key step that contains the diagonal tile
   static constexpr int NTILES = [] {
@@ -559,7 +590,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   using E = typename Cfg::E;
   using frag = typename M::frag;
   constexpr int D = Cfg::D, DV = Cfg::DV, C = Cfg::C, NW = Cfg::NW, G = Cfg::G;
-  constexpr int FT = Cfg::FT, QT = Cfg::QT, KSC = Cfg::KSC, KSF = Cfg::KSF;
+  constexpr int QT = Cfg::QT, KSC = Cfg::KSC, NDT = Cfg::NDT, FTG = Cfg::FTG, KSG = Cfg::KSG, KZ0 = Cfg::KZ0;
   constexpr bool MAIN = MODE == MODE_MAIN;
 
   __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
@@ -571,9 +602,17 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   KE* sPK = reinterpret_cast<KE*>(smem + Cfg::OFF_PK);
   E* sP = reinterpret_cast<E*>(smem + Cfg::OFF_P);
   float* sDen = reinterpret_cast<float*>(smem + Cfg::OFF_DEN);
+  f32x4* sRed = reinterpret_cast<f32x4*>(smem + Cfg::OFF_RED);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // wave index in a scalar register: branches on it around MFMAs must be
+  // scalar branches (an MFMA ignores the exec mask)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // split z: dv pair dg (value tiles 2 dg, 2 dg + 1) of feature group fg
+  const int dg = Cfg::ZS ? (w & 1) : 0;
+  const int fg = Cfg::ZS ? (w >> 1) : 0;
+  const int vt0 = Cfg::ZS ? NDT * dg : w;  // first value tile (16 columns of dv)
+  const int ftg0 = fg * FTG;               // first feature tile of the group
   const int lane = tid & 63;
   const int g4 = lane >> 4;
   const int c = lane & 15;
@@ -605,46 +644,74 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     sV[(DV + 1) * Cfg::PK + i] = M::cvt(0.f);
 
   // ---- initial state of this slice ------------------------------------------
-  f32x4 S[FT];
+  // S[j][ft]: value tile vt0 + j (without split z, on the last wave: the
+  // ones column) of feature tile ftg0 + ft. Z (split z): the ones column of
+  // the slice's feature tiles zlo .. zlo + nzt - 1.
+  constexpr int ZT = Cfg::ZT, TPW = Cfg::TPW;
+  const int zlo = Cfg::ZS ? 2 * (fg * KSG + (dg == 0 ? 0 : KZ0)) : 0;
+  const int nzt = Cfg::ZS ? 2 * (dg == 0 ? KZ0 : KSG - KZ0) : 0;
+  f32x4 S[NDT][FTG];
+  f32x4 Z[ZT > 0 ? ZT : 1];
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) S[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NDT; ++j)
+#pragma unroll
+    for (int ft = 0; ft < FTG; ++ft) S[j][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < (ZT > 0 ? ZT : 1); ++j) Z[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if constexpr (MAIN) {
     if (a.S0 != nullptr) {
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
+      for (int j = 0; j < NDT; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = f0 + 16 * ft + 4 * g4 + i;
-          float val = 0.f;
-          if (f < Cfg::F) {
-            if (w < NW - 1)
-              val = a.S0[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c];
-            else if (c == 0)
-              val = a.z0[static_cast<size_t>(bh) * Cfg::F + f];
-            if constexpr (!Cfg::UNROLL) val /= state_scale<Cfg>(f);
+        for (int ft = 0; ft < FTG; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 16 * (ftg0 + ft) + 4 * g4 + i;
+            float val = 0.f;
+            if (f < Cfg::F) {
+              if (Cfg::ZS || w < NW - 1)
+                val = a.S0[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * (vt0 + j) + c];
+              else if (c == 0)
+                val = a.z0[static_cast<size_t>(bh) * Cfg::F + f];
+              if constexpr (!Cfg::UNROLL) val /= state_scale<Cfg>(f);
+            }
+            S[j][ft][i] = val;
           }
-          S[ft][i] = val;
-        }
+      if constexpr (Cfg::ZS) {
+#pragma unroll
+        for (int jz = 0; jz < ZT; ++jz)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 16 * (zlo + jz) + 4 * g4 + i;
+            Z[jz][i] = (c == 0 && jz < nzt && f < Cfg::F)
+                           ? a.z0[static_cast<size_t>(bh) * Cfg::F + f] / state_scale<Cfg>(f)
+                           : 0.f;
+          }
+      }
       if (EXT && p > 0) {
         // S0 is the state just before token 0; this segment starts at t0
         const float g0 = exp2f(static_cast<float>(p) * static_cast<float>(a.L) * a.log2g);
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) S[ft] *= g0;
+        for (int j = 0; j < NDT; ++j)
+#pragma unroll
+          for (int ft = 0; ft < FTG; ++ft) S[j][ft] *= g0;
+#pragma unroll
+        for (int jz = 0; jz < ZT; ++jz) Z[jz] *= g0;
       }
     }
     // sum of the earlier segments' states, PB segments' loads in flight at once
     const int PS = a.P - 1;
-    constexpr int PB = FT <= 10 ? 4 : (FT <= 20 ? 2 : 1);
+    constexpr int PB = TPW <= 10 ? 4 : (TPW <= 20 ? 2 : 1);
     for (int pp = 0; pp < p; pp += PB) {
-      f32x4 t[PB][FT];
+      f32x4 t[PB][TPW];
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
         // segments past p - 1 re-read segment pp (in bounds) and are dropped
         const int ps = pp + j < p ? pp + j : pp;
         const f32x4* src = reinterpret_cast<const f32x4*>(a.seg) +
-                           ((((static_cast<size_t>(bh) * PS + ps) * G + gsl) * NW + w) * FT) * 64 + lane;
+                           ((((static_cast<size_t>(bh) * PS + ps) * G + gsl) * NW + w) * TPW) * 64 + lane;
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) t[j][ft] = src[ft * 64];
+        for (int ft = 0; ft < TPW; ++ft) t[j][ft] = src[ft * 64];
       }
 #pragma unroll
       for (int j = 0; j < PB; ++j)
@@ -653,7 +720,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           const float gq = EXT ? exp2f(static_cast<float>(p - 1 - pp - j) * static_cast<float>(a.L) * a.log2g)
                                    : 1.f;
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft) S[ft] += gq * t[j][ft];
+          for (int jj = 0; jj < NDT; ++jj)
+#pragma unroll
+            for (int ft = 0; ft < FTG; ++ft) S[jj][ft] += gq * t[j][jj * FTG + ft];
+#pragma unroll
+          for (int zj = 0; zj < ZT; ++zj) Z[zj] += gq * t[j][NDT * FTG + zj];
         }
     }
   }
@@ -769,6 +840,14 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       }
     }
     for (int i = tid; i < C; i += Cfg::NTHR) sV[DV * Cfg::PK + i] = M::cvt(i < nvv ? 1.f : 0.f);
+    if constexpr (Cfg::ZS) {
+      // row 0 of the factor tables, again for every chunk: their space holds
+      // the read-out partials from the feature generation to the chunk's end
+      for (int t = tid; t < C; t += Cfg::NTHR) {
+        sTQ[t] = 1.f;
+        sTK[t] = static_cast<KE>(1.f);
+      }
+    }
   };
 
   if (t0 < t1) fetch(t0);
@@ -815,45 +894,85 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    // [V,1]^T fragments of this wave's dv tile (A operand of the intra-chunk
-    // term, B operand of the state update).
-    frag bv[KSC];
+    // [V,1]^T fragments of the wave's value tiles (A operand of the
+    // intra-chunk term, B operand of the state update)
+    frag bv[NDT][KSC];
 #pragma unroll
-    for (int u = 0; u < KSC; ++u) bv[u] = lds_frag8(sV + (16 * w + c) * Cfg::PK + 32 * u + 8 * g4);
+    for (int j = 0; j < NDT; ++j)
+#pragma unroll
+      for (int u = 0; u < KSC; ++u) bv[j][u] = lds_frag8(sV + (16 * (vt0 + j) + c) * Cfg::PK + 32 * u + 8 * g4);
+    // split z: the ones row of [V,1]^T (and zero rows below it), the B
+    // operand of the z update and the A operand of the intra-chunk
+    // denominator
+    frag bo[KSC];
+    if constexpr (Cfg::ZS) {
+#pragma unroll
+      for (int u = 0; u < KSC; ++u) bo[u] = lds_frag8(sV + (DV + c) * Cfg::PK + 32 * u + 8 * g4);
+    }
 
     if (want_out) {
-      // read-out of the state: O^T[dv tile w] = S^T phi~(Q)^T. The phi~(Q)
-      // fragments of k-step t+1 are fetched before the MFMAs of k-step t.
-      f32x4 acc[QT];
+      // read-out of the state over the wave's feature group: O^T[value tile]
+      // = S^T phi~(Q)^T. Each phi~(Q) fragment feeds the wave's NDT value
+      // tiles and, on the wave's z k-steps, the z tile (row 0 of accZ is
+      // the denominator); the fragments of k-step t+1 are fetched before
+      // the MFMAs of k-step t.
+      f32x4 acc[NDT][QT], accZ[QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) acc[j][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accZ[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const E* pq = sPQ + 32 * fg * KSG + 4 * g4;
       frag bq[2][QT];
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) bq[0][qt] = lds_frag_split(sPQ + (16 * qt + c) * Cfg::PQ + 4 * g4);
+      for (int qt = 0; qt < QT; ++qt) bq[0][qt] = lds_frag_split(pq + (16 * qt + c) * Cfg::PQ);
 #pragma unroll
-      for (int t = 0; t < KSF; ++t) {
-        if (t + 1 < KSF) {
+      for (int t = 0; t < KSG; ++t) {
+        if (t + 1 < KSG) {
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt)
-            bq[(t + 1) & 1][qt] = lds_frag_split(sPQ + (16 * qt + c) * Cfg::PQ + 32 * (t + 1) + 4 * g4);
-        }
-        frag sa;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sa[j] = M::cvt(S[2 * t][j]);
-          sa[j + 4] = M::cvt(S[2 * t + 1][j]);
+            bq[(t + 1) & 1][qt] = lds_frag_split(pq + (16 * qt + c) * Cfg::PQ + 32 * (t + 1));
         }
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt] = M::step(sa, bq[t & 1][qt], acc[qt]);
+        for (int j = 0; j < NDT; ++j) {
+          frag sa;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sa[i] = M::cvt(S[j][2 * t][i]);
+            sa[i + 4] = M::cvt(S[j][2 * t + 1][i]);
+          }
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) acc[j][qt] = M::step(sa, bq[t & 1][qt], acc[j][qt]);
+        }
+        if constexpr (Cfg::ZS) {
+          // k-step t of the group: z of dv pair 0 if t < KZ0, else of pair 1
+          if ((t < KZ0) == (dg == 0)) {
+            const int jz = 2 * (t < KZ0 ? t : t - KZ0);
+            frag za;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              za[i] = M::cvt(Z[jz][i]);
+              za[i + 4] = M::cvt(Z[jz + 1][i]);
+            }
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) accZ[qt] = M::step(za, bq[t & 1][qt], accZ[qt]);
+          }
+        }
       }
       if constexpr (EXT) {
         // the state read out by query i of the chunk is i + 1 steps old
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt] *= exp2f(static_cast<float>(16 * qt + c + 1) * a.log2g);
+        for (int qt = 0; qt < QT; ++qt) {
+          const float gq = exp2f(static_cast<float>(16 * qt + c + 1) * a.log2g);
+#pragma unroll
+          for (int j = 0; j < NDT; ++j) acc[j][qt] *= gq;
+          accZ[qt] *= gq;
+        }
       }
-      // intra-chunk term: O^T += [V,1]^T P^T (first slice only); all P^T
-      // fragments are fetched before the MFMAs.
-      if (gsl == 0) {
+      // intra-chunk term: O^T += [V,1]^T P^T (first slice, first feature
+      // group); all P^T fragments are fetched before the MFMAs.
+      if (gsl == 0 && fg == 0) {
         constexpr int NPF = [] {
           int n = 0;
           for (int qt = 0; qt < QT; ++qt) n += qt / 2 + 1;
@@ -873,104 +992,185 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           constexpr int base = [] { int n = 0; for (int q2 = 0; q2 < qt; ++q2) n += q2 / 2 + 1; return n; }();
           static_for<0, qt / 2 + 1>([&](auto ui) {
             constexpr int u = decltype(ui)::value;
-            acc[qt] = M::step(bv[u], bp[base + u], acc[qt]);
+#pragma unroll
+            for (int j = 0; j < NDT; ++j) acc[j][qt] = M::step(bv[j][u], bp[base + u], acc[j][qt]);
+            // split z: wave 0 adds the intra-chunk denominator (ones row)
+            if (Cfg::ZS && w == 0) accZ[qt] = M::step(bo[u], bp[base + u], accZ[qt]);
           });
         });
       }
-      if constexpr (G == 1) {
-        // denominator: row DV of O^T = wave NW-1, lane group 0, element 0
+      if constexpr (Cfg::ZS) {
+        // feature groups 1 .. NFG-1 hand their value partials to group 0,
+        // every wave its share of the denominator
+        if (fg > 0) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int j = 0; j < NDT; ++j)
+              sRed[(((fg - 1) * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane] = acc[j][qt];
+        }
+        if (g4 == 0) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) sDen[w * C + 16 * qt + c] = accZ[qt][0];
+        }
+        __syncthreads();
+        if (fg == 0) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+            for (int g = 0; g < Cfg::NFG - 1; ++g)
+#pragma unroll
+              for (int j = 0; j < NDT; ++j) acc[j][qt] += sRed[((g * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane];
+            float dsum = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) dsum += sDen[ww * C + 16 * qt + c];
+            accZ[qt][0] = dsum;
+          }
+        }
+      } else if constexpr (G == 1) {
+        // denominator: row DV of O^T (wave NW-1, lane group 0, element 0)
         if (w == NW - 1 && g4 == 0) {
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) sDen[16 * qt + c] = acc[qt][0];
+          for (int qt = 0; qt < QT; ++qt) sDen[16 * qt + c] = acc[0][qt][0];
         }
         __syncthreads();
         if (w < NW - 1) {
 #pragma unroll
+          for (int qt = 0; qt < QT; ++qt) accZ[qt][0] = sDen[16 * qt + c];
+        }
+      }
+      if (Cfg::ZS ? fg == 0 : (w < NW - 1 || G > 1)) {
+        if constexpr (G == 1) {
+#pragma unroll
           for (int qt = 0; qt < QT; ++qt) {
             const int qi = 16 * qt + c;
             if (qi < nv) {
-              const float r = 1.f / sDen[qi];
-              const size_t off = (static_cast<size_t>(bh) * N + c0 + qi) * DV + 16 * w + 4 * g4;
-              if (a.out_bf16) {
-                bf16x4 ov;
+              const float r = 1.f / accZ[qt][0];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(acc[qt][i] * r);
-                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
-              } else {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = acc[qt] * r;
+              for (int j = 0; j < NDT; ++j) {
+                const size_t off = (static_cast<size_t>(bh) * N + c0 + qi) * DV + 16 * (vt0 + j) + 4 * g4;
+                if (a.out_bf16) {
+                  bf16x4 ov;
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(acc[j][qt][i] * r);
+                  *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
+                } else {
+                  *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = acc[j][qt] * r;
+                }
               }
             }
           }
-        }
-      } else {
-        float* pp = a.part + ((static_cast<size_t>(gsl) * a.BH + bh) * N + c0) * Cfg::PPITCH;
+        } else {
+          // partial rows: the value tiles, and the denominator in column DV
+          float* pp = a.part + ((static_cast<size_t>(gsl) * a.BH + bh) * N + c0) * Cfg::PPITCH;
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const int qi = 16 * qt + c;
-          if (qi < nv) {
-            if (w < NW - 1)
-              *reinterpret_cast<f32x4*>(pp + qi * Cfg::PPITCH + 16 * w + 4 * g4) = acc[qt];
-            else if (g4 == 0)
-              pp[qi * Cfg::PPITCH + DV] = acc[qt][0];
+          for (int qt = 0; qt < QT; ++qt) {
+            const int qi = 16 * qt + c;
+            if (qi < nv) {
+              if (Cfg::ZS || w < NW - 1) {
+#pragma unroll
+                for (int j = 0; j < NDT; ++j)
+                  *reinterpret_cast<f32x4*>(pp + qi * Cfg::PPITCH + 16 * (vt0 + j) + 4 * g4) = acc[j][qt];
+              }
+              if (Cfg::ZS ? (w == 0 && g4 == 0) : (w == NW - 1 && g4 == 0))
+                pp[qi * Cfg::PPITCH + DV] = Cfg::ZS ? accZ[qt][0] : acc[0][qt][0];
+            }
           }
         }
       }
     }
 
     if (do_update) {
-      // S[:, dv tile w] += phi(K)^T [V,1][:, dv tile w]; the phi(K)^T
-      // fragments of feature tile ft+1 are fetched before the MFMAs of ft.
-      // With a decay: S = g^nv S + sum_j g^(nv-1-j) phi(k_j) [v_j, 1].
-      frag bu[KSC];
+      // S[value tile, feature tile] += phi(K)^T [V,1]: each phi(K)^T fragment
+      // feeds the wave's NDT value tiles and, on the wave's z tiles, the z
+      // tile; the fragments of feature tile ft+1 are fetched before the
+      // MFMAs of ft. With a decay: S = g^nv S + sum_j g^(nv-1-j) phi(k_j) [v_j, 1].
+      frag bu[NDT][KSC], buo[KSC];
 #pragma unroll
-      for (int u = 0; u < KSC; ++u) bu[u] = bv[u];
+      for (int u = 0; u < KSC; ++u) {
+#pragma unroll
+        for (int j = 0; j < NDT; ++j) bu[j][u] = bv[j][u];
+        if constexpr (Cfg::ZS) buo[u] = bo[u];
+      }
       if constexpr (EXT) {
         const float gs = exp2f(static_cast<float>(nv) * a.log2g);
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) S[ft] *= gs;
+        for (int j = 0; j < NDT; ++j)
+#pragma unroll
+          for (int ft = 0; ft < FTG; ++ft) S[j][ft] *= gs;
+#pragma unroll
+        for (int jz = 0; jz < ZT; ++jz) Z[jz] *= gs;
 #pragma unroll
         for (int u = 0; u < KSC; ++u)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int key = 32 * u + 8 * g4 + j;
+          for (int i = 0; i < 8; ++i) {
+            const int key = 32 * u + 8 * g4 + i;
             const float f = key < nv ? exp2f(static_cast<float>(nv - 1 - key) * a.log2g) : 0.f;
-            bu[u][j] = M::cvt(static_cast<float>(bv[u][j]) * f);
+#pragma unroll
+            for (int j = 0; j < NDT; ++j) bu[j][u][i] = M::cvt(static_cast<float>(bv[j][u][i]) * f);
+            if constexpr (Cfg::ZS) buo[u][i] = M::cvt(static_cast<float>(bo[u][i]) * f);
           }
       }
+      // k-steps of the z update: feature tile ft of the group is a z tile of
+      // dv pair 0 if ft < 2 KZ0, else of pair 1
+      auto zmine = [&](int ft) { return (ft < 2 * KZ0) == (dg == 0); };
+      auto zidx = [&](int ft) { return ft < 2 * KZ0 ? ft : ft - 2 * KZ0; };
       if constexpr (Cfg::KH) {
         // fp16 contraction: u(KS K)^T from the key table, [V,1] converted
-        f16x8 bvh[KSC], ak[2][KSC];
+        f16x8 bvh[NDT][KSC], boh[KSC], ak[2][KSC];
 #pragma unroll
-        for (int u = 0; u < KSC; ++u)
+        for (int u = 0; u < KSC; ++u) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) bvh[u][j] = static_cast<_Float16>(static_cast<float>(bu[u][j]));
+          for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int u = 0; u < KSC; ++u) ak[0][u] = *reinterpret_cast<const f16x8*>(sPK + c * Cfg::PK + 32 * u + 8 * g4);
+            for (int j = 0; j < NDT; ++j) bvh[j][u][i] = static_cast<_Float16>(static_cast<float>(bu[j][u][i]));
+            if constexpr (Cfg::ZS) boh[u][i] = static_cast<_Float16>(static_cast<float>(buo[u][i]));
+          }
+        }
+        const KE* pk = sPK + (16 * ftg0 + c) * Cfg::PK + 8 * g4;
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) {
-          if (ft + 1 < FT) {
+        for (int u = 0; u < KSC; ++u) ak[0][u] = *reinterpret_cast<const f16x8*>(pk + 32 * u);
+#pragma unroll
+        for (int ft = 0; ft < FTG; ++ft) {
+          if (ft + 1 < FTG) {
 #pragma unroll
             for (int u = 0; u < KSC; ++u)
-              ak[(ft + 1) & 1][u] =
-                  *reinterpret_cast<const f16x8*>(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
+              ak[(ft + 1) & 1][u] = *reinterpret_cast<const f16x8*>(pk + 16 * (ft + 1) * Cfg::PK + 32 * u);
           }
 #pragma unroll
-          for (int u = 0; u < KSC; ++u)
-            S[ft] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ft & 1][u], bvh[u], S[ft], 0, 0, 0);
+          for (int j = 0; j < NDT; ++j)
+#pragma unroll
+            for (int u = 0; u < KSC; ++u)
+              S[j][ft] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ft & 1][u], bvh[j][u], S[j][ft], 0, 0, 0);
+          if constexpr (Cfg::ZS) {
+            if (zmine(ft)) {
+#pragma unroll
+              for (int u = 0; u < KSC; ++u)
+                Z[zidx(ft)] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[ft & 1][u], boh[u], Z[zidx(ft)], 0, 0, 0);
+            }
+          }
         }
       } else {
         frag ak[2][KSC];
+        const KE* pk = sPK + (16 * ftg0 + c) * Cfg::PK + 8 * g4;
 #pragma unroll
-        for (int u = 0; u < KSC; ++u) ak[0][u] = lds_frag8(sPK + c * Cfg::PK + 32 * u + 8 * g4);
+        for (int u = 0; u < KSC; ++u) ak[0][u] = lds_frag8(pk + 32 * u);
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) {
-          if (ft + 1 < FT) {
+        for (int ft = 0; ft < FTG; ++ft) {
+          if (ft + 1 < FTG) {
 #pragma unroll
-            for (int u = 0; u < KSC; ++u)
-              ak[(ft + 1) & 1][u] = lds_frag8(sPK + (16 * (ft + 1) + c) * Cfg::PK + 32 * u + 8 * g4);
+            for (int u = 0; u < KSC; ++u) ak[(ft + 1) & 1][u] = lds_frag8(pk + 16 * (ft + 1) * Cfg::PK + 32 * u);
           }
 #pragma unroll
-          for (int u = 0; u < KSC; ++u) S[ft] = M::step(ak[ft & 1][u], bu[u], S[ft]);
+          for (int j = 0; j < NDT; ++j)
+#pragma unroll
+            for (int u = 0; u < KSC; ++u) S[j][ft] = M::step(ak[ft & 1][u], bu[j][u], S[j][ft]);
+          if constexpr (Cfg::ZS) {
+            if (zmine(ft)) {
+#pragma unroll
+              for (int u = 0; u < KSC; ++u) Z[zidx(ft)] = M::step(ak[ft & 1][u], buo[u], Z[zidx(ft)]);
+            }
+          }
         }
       }
     }
@@ -978,39 +1178,57 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- results ---------------------------------------------------------------
+  // staged states (segment sums, deferred final state): per (unit, slice)
+  // and wave, TPW tiles of 64 lanes: the NDT x FTG value tiles, then the ZT
+  // z tiles
+  auto store_tiles = [&](f32x4* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NDT; ++j)
+#pragma unroll
+      for (int ft = 0; ft < FTG; ++ft) dst[(j * FTG + ft) * 64] = S[j][ft];
+#pragma unroll
+    for (int jz = 0; jz < ZT; ++jz) dst[(NDT * FTG + jz) * 64] = Z[jz];
+  };
   if constexpr (MAIN) {
     if (want_state && a.defer_state) {
-      f32x4* dst = reinterpret_cast<f32x4*>(a.fin) +
-                   (((static_cast<size_t>(bh) * G + gsl) * NW + w) * FT) * 64 + lane;
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) dst[ft * 64] = S[ft];
+      store_tiles(reinterpret_cast<f32x4*>(a.fin) + (((static_cast<size_t>(bh) * G + gsl) * NW + w) * TPW) * 64 + lane);
     } else if (want_state) {
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft)
+      for (int j = 0; j < NDT; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = f0 + 16 * ft + 4 * g4 + i;
-          if (f < Cfg::F) {
-            const float sc = state_scale<Cfg>(f);
-            if (w < NW - 1)
-              a.S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = sc * S[ft][i];
-            else if (c == 0)
-              a.z[static_cast<size_t>(bh) * Cfg::F + f] = sc * S[ft][i];
+        for (int ft = 0; ft < FTG; ++ft)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 16 * (ftg0 + ft) + 4 * g4 + i;
+            if (f < Cfg::F) {
+              const float sc = state_scale<Cfg>(f);
+              if (Cfg::ZS || w < NW - 1)
+                a.S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * (vt0 + j) + c] = sc * S[j][ft][i];
+              else if (c == 0)
+                a.z[static_cast<size_t>(bh) * Cfg::F + f] = sc * S[j][ft][i];
+            }
           }
-        }
+      if constexpr (Cfg::ZS) {
+#pragma unroll
+        for (int jz = 0; jz < ZT; ++jz)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int f = f0 + 16 * (zlo + jz) + 4 * g4 + i;
+            if (c == 0 && jz < nzt && f < Cfg::F)
+              a.z[static_cast<size_t>(bh) * Cfg::F + f] = state_scale<Cfg>(f) * Z[jz][i];
+          }
+      }
     }
   } else {
     const int PS = a.P - 1;
-    f32x4* dst = reinterpret_cast<f32x4*>(a.seg) +
-                 ((((static_cast<size_t>(bh) * PS + p) * G + gsl) * NW + w) * FT) * 64 + lane;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) dst[ft * 64] = S[ft];
+    store_tiles(reinterpret_cast<f32x4*>(a.seg) +
+                ((((static_cast<size_t>(bh) * PS + p) * G + gsl) * NW + w) * TPW) * 64 + lane);
   }
 }
 
 // Sum the per-slice partial (numerator, denominator) rows and divide.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int G,
-                                                      int64_t rows, int dv, int pitch, void* o,
+                                                      int64_t rows, int dv, int pitch, int nden, void* o,
                                                       int out_bf16) {
   const int nq = dv / 4;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -1022,7 +1240,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int g = 0; g < G; ++g) {
     const float* src = part + (static_cast<int64_t>(g) * rows + r) * pitch;
     num += *reinterpret_cast<const f32x4*>(src + 4 * dq);
-    den += src[dv];
+    for (int j = 0; j < nden; ++j) den += src[dv + j];  // denominator shares of the waves
   }
   const float rcp = 1.f / den;
   const int64_t off = r * dv + 4 * dq;
@@ -1048,22 +1266,37 @@ __global__ __launch_bounds__(256) void state_init_kernel(const float* S0, const 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NTHR) void state_store_kernel(const float* fin, float* S, float* z,
                                                                 int BH) {
-  constexpr int NW = Cfg::NW, FT = Cfg::FT, G = Cfg::G, DV = Cfg::DV;
+  constexpr int NW = Cfg::NW, NDT = Cfg::NDT, FTG = Cfg::FTG, KSG = Cfg::KSG, KZ0 = Cfg::KZ0, G = Cfg::G;
+  constexpr int DV = Cfg::DV, TPW = Cfg::TPW;
   const int bh = blockIdx.x / G, gsl = blockIdx.x % G;
   if (bh >= BH) return;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g4 = lane >> 4, c = lane & 15;
+  const int dg = Cfg::ZS ? (w & 1) : 0, fg = Cfg::ZS ? (w >> 1) : 0;
+  const int vt0 = Cfg::ZS ? NDT * dg : w, ftg0 = fg * FTG;
   const f32x4* src = reinterpret_cast<const f32x4*>(fin) +
-                     (((static_cast<size_t>(bh) * G + gsl) * NW + w) * FT) * 64 + lane;
-  for (int ft = 0; ft < FT; ++ft) {
-    const f32x4 val = src[ft * 64];
-    for (int i = 0; i < 4; ++i) {
-      const int f = gsl * Cfg::FS + 16 * ft + 4 * g4 + i;
-      if (f < Cfg::F) {
-        const float sc = state_scale<Cfg>(f);
-        if (w < NW - 1)
-          S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * w + c] = sc * val[i];
-        else if (c == 0)
-          z[static_cast<size_t>(bh) * Cfg::F + f] = sc * val[i];
+                     (((static_cast<size_t>(bh) * G + gsl) * NW + w) * TPW) * 64 + lane;
+  for (int j = 0; j < NDT; ++j)
+    for (int ft = 0; ft < FTG; ++ft) {
+      const f32x4 val = src[(j * FTG + ft) * 64];
+      for (int i = 0; i < 4; ++i) {
+        const int f = gsl * Cfg::FS + 16 * (ftg0 + ft) + 4 * g4 + i;
+        if (f < Cfg::F) {
+          const float sc = state_scale<Cfg>(f);
+          if (Cfg::ZS || w < NW - 1)
+            S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * (vt0 + j) + c] = sc * val[i];
+          else if (c == 0)
+            z[static_cast<size_t>(bh) * Cfg::F + f] = sc * val[i];
+        }
+      }
+    }
+  if constexpr (Cfg::ZS) {
+    // split z: the wave's z tiles (column 0 of each)
+    const int zlo = 2 * (fg * KSG + (dg == 0 ? 0 : KZ0)), nzt = 2 * (dg == 0 ? KZ0 : KSG - KZ0);
+    for (int jz = 0; jz < nzt; ++jz) {
+      const f32x4 val = src[(NDT * FTG + jz) * 64];
+      for (int i = 0; i < 4; ++i) {
+        const int f = gsl * Cfg::FS + 16 * (zlo + jz) + 4 * g4 + i;
+        if (c == 0 && f < Cfg::F) z[static_cast<size_t>(bh) * Cfg::F + f] = state_scale<Cfg>(f) * val[i];
       }
     }
   }
@@ -1106,7 +1339,7 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
     const int64_t rows = static_cast<int64_t>(a.BH) * a.N;
     const int64_t n = rows * (Cfg::DV / 4);
     hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
-                       a.part, G, rows, Cfg::DV, Cfg::PPITCH, a.o, a.out_bf16);
+                       a.part, G, rows, Cfg::DV, Cfg::PPITCH, Cfg::NDEN, a.o, a.out_bf16);
     e = hipGetLastError();
   }
   return e;
@@ -1124,9 +1357,9 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(16, 64, 3, false, 160, 64, true)        \
   X(16, 16, 5, true, 608, 32, false)        \
   X(16, 16, 5, false, 256, 32, false)       \
-  X(16, 64, 5, true, 608, 32, false)        \
+  X(16, 64, 5, true, 640, 32, false)        \
   X(16, 64, 5, false, 256, 32, false)       \
-  X(16, 64, 7, true, 608, 32, false)        \
+  X(16, 64, 7, true, 640, 32, false)        \
   X(16, 64, 7, false, 256, 32, false)       \
   X(32, 16, 1, true, 32, 64, true)          \
   X(32, 16, 1, false, 32, 64, true)         \
@@ -1134,7 +1367,7 @@ static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   X(32, 64, 1, false, 32, 64, true)         \
   X(32, 16, 3, true, 576, 32, false)        \
   X(32, 16, 3, false, 128, 32, false)       \
-  X(32, 64, 3, true, 288, 32, false)        \
+  X(32, 64, 3, true, 640, 32, false)        \
   X(32, 64, 3, false, 128, 32, false)       \
   X(64, 16, 1, true, 32, 64, true)          \
   X(64, 16, 1, false, 32, 64, true)         \
@@ -1167,13 +1400,14 @@ static void plan_cfg(int BH, int N, PrefillPlan* p) {
   const int64_t cps = (nchunks + P - 1) / P;
   p->L = static_cast<int>(cps * C);
   p->P = static_cast<int>((nchunks + cps - 1) / cps);
-  const size_t FP = static_cast<size_t>(Cfg::G) * Cfg::FS;
+  // staged states: G slices x SLICE_F4 float4s per (head, segment)
+  const size_t UB = static_cast<size_t>(Cfg::G) * Cfg::SLICE_F4 * 16;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t off = 0;
   p->seg_off = off;
-  if (p->P > 1) off += al(static_cast<size_t>(BH) * (p->P - 1) * FP * Cfg::DVP * 4);
+  if (p->P > 1) off += al(static_cast<size_t>(BH) * (p->P - 1) * UB);
   p->fin_off = off;
-  if (p->P > 1) off += al(static_cast<size_t>(BH) * FP * Cfg::DVP * 4);
+  if (p->P > 1) off += al(static_cast<size_t>(BH) * UB);
   p->part_off = off;
   if (Cfg::G > 1) off += al(static_cast<size_t>(Cfg::G) * BH * static_cast<size_t>(N) * Cfg::PPITCH * 4);
   p->bytes = off;

@@ -91,7 +91,7 @@ def test_prefill_order6_small(dtype, N, qk):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_order6_multi_segment(dtype):
     # long enough for several segments (the split targets about 512
-    # workgroups over heads x segments x 123 feature slices)
+    # workgroups over heads x segments x 117 feature slices)
     B, H, N = 1, 1, 3000
     x = W.make_qkv(B, H, N, D, DV, dtype, 607, "l2x2")
     say("order-6 prefill multi-segment", dtype)
