@@ -126,7 +126,13 @@ struct PCfg {
   // carries the sqrt-multinomial weight, so that internal and canonical
   // state rows differ by KS^m only
   static constexpr bool TRIPLE = NT > 5;
-  static constexpr int TE = UNROLL ? 0 : 1 + D + (PAIRS ? D * (D + 1) / 2 : 0);
+  // order 4 at d = 16 with bf16 inputs: the query features are generated
+  // per token with compile-time indices (one code path per slice and wave)
+  // and only the key side keeps a factor table
+  static constexpr bool QGEN = BF16 && !UNROLL && D == 16 && NT == 5 && C == 32 && DV == 64;
+  static constexpr bool TAB = !UNROLL;  // factor tables (key side; query side unless QGEN)
+  static constexpr int TE = TAB ? 1 + D + (PAIRS ? D * (D + 1) / 2 : 0) : 0;
+  static constexpr int TQE = QGEN ? 0 : TE;  // query table rows
   static constexpr int TP = C + 4;
   // key side of the table-driven generator: bf16 inputs keep the key table,
   // phi(K)^T and the update contraction in fp16 (keys scaled by KS, so
@@ -137,7 +143,7 @@ struct PCfg {
   static constexpr int TPK = KH ? C + 8 : C + 4;
   // (split z: the denominator shares of all waves, [NW][C])
   static constexpr int OFF_TQ = OFF_DEN + (ZS_() ? NW : 1) * C * 4;
-  static constexpr int OFF_TK = OFF_TQ + TE * TP * 4;
+  static constexpr int OFF_TK = OFF_TQ + TQE * TP * 4;
   static constexpr int TAB_END = OFF_TK + TE * TPK * KES;
   // split z: the read-out partials of feature groups 1 .. NFG-1 ([NFG-1][C]
   // [DV], f32x4 per lane and tile) reuse the factor tables, which are dead
@@ -152,6 +158,7 @@ struct PCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(DV + NDEN <= PPITCH, "partial-output row holds the values and the denominator columns");
   static_assert(!ZS || (FS % (32 * NFG) == 0 && DV == 16 * NDT * (NW / NFG)), "split z: whole k-steps per group");
+  static_assert(!QGEN || (ZS && FS % (8 * NW) == 0), "per-token generator: whole 8-feature packs per wave");
   // score tiles (kt, qt) needed per chunk: key tiles up to the end of the
   // 32-key step that contains the diagonal tile
   static constexpr int NTILES = [] {
@@ -251,6 +258,73 @@ __device__ __forceinline__ void gen_unrolled(int w, const float (&x)[Cfg::D], ty
         gen_q_packs<Cfg, PB, PE>(x, dst);
       else
         gen_k_packs<Cfg, PB, PE>(x, dst);
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// query features per token with compile-time indices (order 4, d = 16)
+// ---------------------------------------------------------------------------
+// Lane t < 32 of a wave generates the query features of token t of the
+// chunk for the wave's FS / NW features of the slice, from its coordinates
+// q / (a KS) held in registers, and stores them as 8-feature packs into the
+// token's row of phi~(Q). The query side carries the whole weight
+// w^2 / m! = 1 / prod_i c_i! (c_i the multiplicities of the tuple), the key
+// side the plain products u(KS k), as on the table path.
+
+template <int D, int NT, int f>
+__device__ __forceinline__ float qfeat_val(const float (&x)[D]) {
+  if constexpr (f >= feature_count(D, NT)) {
+    return 0.f;
+  } else {
+    constexpr Monomial e = kBasis<D, NT>.e[f];
+    if constexpr (e.m == 0) {
+      return 1.f;
+    } else {
+      // left-to-right products: features that share a prefix share its
+      // product after value numbering
+      float p = x[e.idx[0]];
+      static_for<1, e.m>([&](auto jj) { p = p * x[e.idx[decltype(jj)::value]]; });
+      constexpr double r = static_cast<double>(e.mult) / static_cast<double>(factorial(e.m));
+      if constexpr (r != 1.0) p = p * static_cast<float>(r);
+      return p;
+    }
+  }
+}
+
+template <class Cfg, int SL, int W>
+__device__ __forceinline__ void gen_q_wave(const float (&x)[Cfg::D], typename Cfg::E* dq) {
+  constexpr int FW = Cfg::FS / Cfg::NW;
+  static_for<0, FW / 8>([&](auto pi) {
+    constexpr int p = decltype(pi)::value;
+    bf16x8 pk;
+    static_for<0, 8>([&](auto ji) {
+      constexpr int j = decltype(ji)::value;
+      pk[j] = static_cast<__bf16>(qfeat_val<Cfg::D, Cfg::NT, SL * Cfg::FS + W * FW + 8 * p + j>(x));
+    });
+    *reinterpret_cast<bf16x8*>(dq + 8 * p) = pk;
+  });
+}
+
+// phi~(Q) of the slice for one chunk (query-major). The slice and the wave
+// pick one of G x NW straight-line code paths (scalar branches).
+template <class Cfg>
+__device__ __forceinline__ void gen_q_token(int gsl, int w, int lane, const typename Cfg::E* sQ,
+                                            typename Cfg::E* sPQ, float inv_a) {
+  constexpr int D = Cfg::D, FW = Cfg::FS / Cfg::NW;
+  if (lane >= Cfg::C) return;
+  const typename Cfg::E* xr = sQ + lane * Cfg::XP;
+  const float sc = inv_a / Cfg::KS;
+  float x[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) x[j] = static_cast<float>(xr[j]) * sc;
+  static_for<0, Cfg::G>([&](auto si) {
+    constexpr int SL = decltype(si)::value;
+    if (gsl == SL) {
+      static_for<0, Cfg::NW>([&](auto wi) {
+        constexpr int W = decltype(wi)::value;
+        if (w == W) gen_q_wave<Cfg, SL, W>(x, sPQ + lane * Cfg::PQ + W * FW);
+      });
     }
   });
 }
@@ -737,13 +811,13 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   float* sTQ = reinterpret_cast<float*>(smem + Cfg::OFF_TQ);
   KE* sTK = reinterpret_cast<KE*>(smem + Cfg::OFF_TK);
   const PairJobs<Cfg> pj = pair_jobs<Cfg>(tid);
-  if constexpr (!Cfg::UNROLL) {
+  if constexpr (Cfg::TAB) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) tf[j] = tab_feat<Cfg>(f0 + 64 * (w + NW * j) + lane, inv_a);
     // row 0 of both tables is the constant 1 (also for rows past the end of
     // the sequence: their values and ones-row entries are zero)
     for (int t = tid; t < Cfg::C; t += Cfg::NTHR) {
-      sTQ[t] = 1.f;
+      if constexpr (!Cfg::QGEN) sTQ[t] = 1.f;
       sTK[t] = static_cast<KE>(1.f);
     }
   }
@@ -816,7 +890,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
         if (want_out) {
           *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = val;
-          if constexpr (!Cfg::UNROLL) {
+          if constexpr (Cfg::TAB && !Cfg::QGEN) {
             const E* e = reinterpret_cast<const E*>(&val);
 #pragma unroll
             for (int u = 0; u < EV; ++u) sTQ[(1 + col + u) * Cfg::TP + row] = static_cast<float>(e[u]);
@@ -826,7 +900,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         const int j = i - QB;
         const int row = j / (D / EV), col = (j % (D / EV)) * EV;
         *reinterpret_cast<uint4*>(sK + row * Cfg::XP + col) = val;
-        if constexpr (!Cfg::UNROLL) {
+        if constexpr (Cfg::TAB) {
           const E* e = reinterpret_cast<const E*>(&val);
 #pragma unroll
           for (int u = 0; u < EV; ++u) sTK[(1 + col + u) * Cfg::TPK + row] = static_cast<KE>(static_cast<float>(e[u]) * Cfg::KS);
@@ -840,11 +914,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       }
     }
     for (int i = tid; i < C; i += Cfg::NTHR) sV[DV * Cfg::PK + i] = M::cvt(i < nvv ? 1.f : 0.f);
-    if constexpr (Cfg::ZS) {
+    if constexpr (Cfg::ZS && Cfg::TAB) {
       // row 0 of the factor tables, again for every chunk: their space holds
       // the read-out partials from the feature generation to the chunk's end
       for (int t = tid; t < C; t += Cfg::NTHR) {
-        sTQ[t] = 1.f;
+        if constexpr (!Cfg::QGEN) sTQ[t] = 1.f;
         sTK[t] = static_cast<KE>(1.f);
       }
     }
@@ -879,11 +953,16 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         }
       }
     } else {
-      if constexpr (Cfg::PAIRS) {
-        build_pairs<Cfg>(tid, pj, sTQ, sTK, want_out);
-        __syncthreads();
+      // (per-token query features: before the pair rows' barrier, which they
+      // do not need)
+      if constexpr (Cfg::PAIRS) build_pairs<Cfg>(tid, pj, sTQ, sTK, want_out && !Cfg::QGEN);
+      if constexpr (Cfg::QGEN) {
+        if (want_out) gen_q_token<Cfg>(gsl, w, lane, sQ, sPQ, inv_a);
       }
-      if (want_out) gen_tab<Cfg, true>(w, lane, tf, sTQ, sPQ);
+      if constexpr (Cfg::PAIRS) __syncthreads();
+      if constexpr (!Cfg::QGEN) {
+        if (want_out) gen_tab<Cfg, true>(w, lane, tf, sTQ, sPQ);
+      }
       if (do_update) gen_tab<Cfg, false>(w, lane, tf, sTK, sPK);
     }
     if (want_out && gsl == 0) {
