@@ -284,6 +284,7 @@ taylor_status prefill_impl(const void* q, const void* k, const void* v, taylor_d
   args.N = N;
   args.P = p.P;
   args.L = p.L;
+  args.L0 = p.L0;
   args.inv_a = 1.0f / a;
   args.wait_spins = wait_spins();
   // In-place continuation with several segments: the first segment reads S0

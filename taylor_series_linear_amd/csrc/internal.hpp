@@ -13,6 +13,8 @@ namespace tl {
 struct PrefillPlan {
   int P = 1;             // segments per head
   int L = 0;             // tokens per segment (multiple of the chunk length)
+  int L0 = 0;            // generic kernels, two segments [0, L0) and [L0, N)
+                         // with a prefix pass instead of segment sums (0: off)
   size_t seg_off = 0;    // byte offsets into the workspace
   size_t fin_off = 0;
   size_t part_off = 0;
@@ -39,6 +41,7 @@ struct PrefillArgs {
   int N;
   int P;        // segments per head
   int L;        // tokens per segment (multiple of C)
+  int L0;       // see PrefillPlan::L0
   float inv_a;
   int defer_state;  // final state goes through `fin`, then a copy kernel
   // extended options (generic kernel family only)

@@ -706,8 +706,13 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   const bool want_state = MAIN && a.S != nullptr && p == a.P - 1;
   if (MAIN && !want_out && !want_state) return;
 
-  const int t0 = p * a.L;
-  const int t1 = min(N, t0 + a.L);
+  // Segment p holds tokens [t0, t1). With a prefix pass (two segments of
+  // lengths L0 and N - L0) the main launch runs segment 1 from token 0,
+  // updating the state without read-out up to t0: there are no segment sums.
+  const bool prefix_pass = a.L0 > 0;
+  const int t0 = prefix_pass ? (p == 0 ? 0 : a.L0) : p * a.L;
+  const int t1 = prefix_pass ? (p == 0 ? a.L0 : N) : min(N, t0 + a.L);
+  const int lo = (MAIN && prefix_pass) ? 0 : t0;  // first token of the chunk loop
 
   const E* qh = reinterpret_cast<const E*>(a.q) + static_cast<size_t>(bh) * N * D;
   const E* kh = reinterpret_cast<const E*>(a.k) + static_cast<size_t>(bh) * N * D;
@@ -762,9 +767,9 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
                            : 0.f;
           }
       }
-      if (EXT && p > 0) {
-        // S0 is the state just before token 0; this segment starts at t0
-        const float g0 = exp2f(static_cast<float>(p) * static_cast<float>(a.L) * a.log2g);
+      if (EXT && lo > 0) {
+        // S0 is the state just before token 0; the chunk loop starts at lo
+        const float g0 = exp2f(static_cast<float>(lo) * a.log2g);
 #pragma unroll
         for (int j = 0; j < NDT; ++j)
 #pragma unroll
@@ -776,7 +781,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     // sum of the earlier segments' states, PB segments' loads in flight at once
     const int PS = a.P - 1;
     constexpr int PB = TPW <= 10 ? 4 : (TPW <= 20 ? 2 : 1);
-    for (int pp = 0; pp < p; pp += PB) {
+    for (int pp = 0; pp < (prefix_pass ? 0 : p); pp += PB) {
       f32x4 t[PB][TPW];
 #pragma unroll
       for (int j = 0; j < PB; ++j) {
@@ -837,19 +842,21 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   // Buffer resources over this segment's rows (base and size in scalar
   // registers): rows past the segment, and Q when no output is wanted, read
   // as zero without branches.
-  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  // (queries from t0, keys and values from the first token of the loop)
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0), loop_rows = static_cast<uint32_t>(t1 - lo);
   const auto rq = make_rsrc(qh + static_cast<size_t>(t0) * D, want_out ? seg_rows * D * Cfg::ES : 0u);
-  const auto rk = make_rsrc(kh + static_cast<size_t>(t0) * D, seg_rows * D * Cfg::ES);
-  const auto rv = make_rsrc(vh + static_cast<size_t>(t0) * DV, seg_rows * DV * Cfg::ES);
+  const auto rk = make_rsrc(kh + static_cast<size_t>(lo) * D, loop_rows * D * Cfg::ES);
+  const auto rv = make_rsrc(vh + static_cast<size_t>(lo) * DV, loop_rows * DV * Cfg::ES);
   auto fetch = [&](int cc0) {
-    const uint32_t r0 = static_cast<uint32_t>(cc0 - t0);
+    const uint32_t r0 = static_cast<uint32_t>(cc0 - lo);
+    const bool qrows = cc0 >= t0;  // prefix-pass chunks read no queries
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int i = tid + s * Cfg::NTHR;
       pf[s] = uint4{0, 0, 0, 0};
       if (i < QB) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
-        pf[s] = bload16(rq, ((r0 + row) * D + col) * Cfg::ES);
+        if (qrows) pf[s] = bload16(rq, ((static_cast<uint32_t>(cc0 - t0) + row) * D + col) * Cfg::ES);
       } else if (i < QB + NQI) {
         const int j = i - QB;
         const int row = j / (D / EV), col = (j % (D / EV)) * EV;
@@ -867,7 +874,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   // rows: the D / EV consecutive lanes that hold one row sum its squares
   // with lane exchanges, then scale their items.
   const float qhead = (EXT && a.q_head_scale != nullptr) ? a.q_head_scale[bh % a.H] : 1.f;
-  auto stage = [&](int nvv) {
+  auto stage = [&](int nvv, bool ro) {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int i = tid + s * Cfg::NTHR;
@@ -888,7 +895,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       }
       if (i < QB) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
-        if (want_out) {
+        if (ro) {
           *reinterpret_cast<uint4*>(sQ + row * Cfg::XP + col) = val;
           if constexpr (Cfg::TAB && !Cfg::QGEN) {
             const E* e = reinterpret_cast<const E*>(&val);
@@ -924,24 +931,24 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  if (t0 < t1) fetch(t0);
-  for (int c0 = t0; c0 < t1; c0 += C) {
+  if (lo < t1) fetch(lo);
+  for (int c0 = lo; c0 < t1; c0 += C) {
     const int nv = min(C, t1 - c0);
     const bool last_chunk = c0 + C >= t1;
     const bool do_update = !MAIN || !last_chunk || want_state;
+    const bool ro = want_out && c0 >= t0;  // read-out wanted for this chunk
 
-    stage(nv);
+    stage(nv, ro);
     __syncthreads();
-    // next chunk's loads after the barrier: a workgroup barrier waits for
-    // every outstanding global access, so loads issued before it would not
-    // overlap this chunk's work
+    // the next chunk's loads stay in flight through this chunk's work (a
+    // barrier waits for LDS operations only; the next staging waits for them)
     if (!last_chunk) fetch(c0 + C);
 
     // features and score tiles
     if constexpr (Cfg::UNROLL) {
       if (lane < C) {
         float x[D];
-        if (want_out) {
+        if (ro) {
 #pragma unroll
           for (int j = 0; j < D; ++j) x[j] = static_cast<float>(sQ[lane * Cfg::XP + j]) * inv_a;
           gen_unrolled<Cfg, true>(w, x, sPQ + lane * Cfg::PQ);
@@ -955,17 +962,17 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
     } else {
       // (per-token query features: before the pair rows' barrier, which they
       // do not need)
-      if constexpr (Cfg::PAIRS) build_pairs<Cfg>(tid, pj, sTQ, sTK, want_out && !Cfg::QGEN);
+      if constexpr (Cfg::PAIRS) build_pairs<Cfg>(tid, pj, sTQ, sTK, ro && !Cfg::QGEN);
       if constexpr (Cfg::QGEN) {
-        if (want_out) gen_q_token<Cfg>(gsl, w, lane, sQ, sPQ, inv_a);
+        if (ro) gen_q_token<Cfg>(gsl, w, lane, sQ, sPQ, inv_a);
       }
       if constexpr (Cfg::PAIRS) __syncthreads();
       if constexpr (!Cfg::QGEN) {
-        if (want_out) gen_tab<Cfg, true>(w, lane, tf, sTQ, sPQ);
+        if (ro) gen_tab<Cfg, true>(w, lane, tf, sTQ, sPQ);
       }
       if (do_update) gen_tab<Cfg, false>(w, lane, tf, sTK, sPK);
     }
-    if (want_out && gsl == 0) {
+    if (ro && gsl == 0) {
       static_for<0, NW>([&](auto ri) {
         if (w == decltype(ri)::value)
           score_tiles<Cfg, decltype(ri)::value>(sK, sQ, sP, c, g4, inv_a, EXT, a.log2g);
@@ -989,7 +996,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
       for (int u = 0; u < KSC; ++u) bo[u] = lds_frag8(sV + (DV + c) * Cfg::PK + 32 * u + 8 * g4);
     }
 
-    if (want_out) {
+    if (ro) {
       // read-out of the state over the wave's feature group: O^T[value tile]
       // = S^T phi~(Q)^T. Each phi~(Q) fragment feeds the wave's NDT value
       // tiles and, on the wave's z k-steps, the z tile (row 0 of accZ is
@@ -1389,7 +1396,7 @@ template <class Cfg>
 static hipError_t launch_cfg(const PrefillArgs& a, hipStream_t stream) {
   constexpr int G = Cfg::G;
   auto blocks_for = [](int units) { return 8 * G * ((units + 7) / 8); };
-  if (a.P > 1) {
+  if (a.P > 1 && a.L0 == 0) {
     const int units = a.BH * (a.P - 1);
     if (a.decay)
       hipLaunchKernelGGL((prefill_kernel<Cfg, MODE_SEGSUM, true>), dim3(blocks_for(units)), dim3(Cfg::NTHR), 0,
@@ -1470,7 +1477,8 @@ static void plan_cfg(int BH, int N, PrefillPlan* p) {
     p->L = N;
     return;
   }
-  const int64_t target = 512;
+  // eight-wave workgroups (split z) run one per compute unit
+  const int64_t target = Cfg::ZS ? 256 : 512;
   const int64_t want = (target + static_cast<int64_t>(BH) * Cfg::G - 1) / (static_cast<int64_t>(BH) * Cfg::G);
   const int64_t maxp = nchunks / 4 > 1 ? nchunks / 4 : 1;
   int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
@@ -1479,12 +1487,24 @@ static void plan_cfg(int BH, int N, PrefillPlan* p) {
   const int64_t cps = (nchunks + P - 1) / P;
   p->L = static_cast<int>(cps * C);
   p->P = static_cast<int>((nchunks + cps - 1) / cps);
+  if (p->P == 2 && minp <= 1) {
+    // Two segments: no segment-sum launch; the workgroup of segment 1 first
+    // runs the keys of segment 0 without read-out (measured at about 0.6 of
+    // a read-out chunk for order 4), so segment 0 takes the larger share,
+    // L0 ~ N / (2 - RHO), and both workgroups finish together.
+    constexpr double RHO = 0.6;
+    int64_t c0 = static_cast<int64_t>(static_cast<double>(nchunks) / (2.0 - RHO) + 0.5);
+    if (c0 > nchunks - 1) c0 = nchunks - 1;
+    if (c0 < 1) c0 = 1;
+    p->L0 = static_cast<int>(c0 * C);
+    p->L = p->L0;
+  }
   // staged states: G slices x SLICE_F4 float4s per (head, segment)
   const size_t UB = static_cast<size_t>(Cfg::G) * Cfg::SLICE_F4 * 16;
   auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   size_t off = 0;
   p->seg_off = off;
-  if (p->P > 1) off += al(static_cast<size_t>(BH) * (p->P - 1) * UB);
+  if (p->P > 1 && p->L0 == 0) off += al(static_cast<size_t>(BH) * (p->P - 1) * UB);
   p->fin_off = off;
   if (p->P > 1) off += al(static_cast<size_t>(BH) * UB);
   p->part_off = off;
