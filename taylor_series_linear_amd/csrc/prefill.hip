@@ -268,9 +268,9 @@ __device__ __forceinline__ void gen_unrolled(int w, const float (&x)[Cfg::D], ty
 // Lane t < 32 of a wave generates the query features of token t of the
 // chunk for the wave's FS / NW features of the slice, from its coordinates
 // q / (a KS) held in registers, and stores them as 8-feature packs into the
-// token's row of phi~(Q). The query side carries the whole weight
-// w^2 / m! = 1 / prod_i c_i! (c_i the multiplicities of the tuple), the key
-// side the plain products u(KS k), as on the table path.
+// token's row of phi~(Q). The query features are plain products; the key
+// side (table path) carries the weight w^2 / m! = 1 / prod_i c_i! (c_i the
+// multiplicities of the tuple), one packed multiply per eight keys.
 
 template <int D, int NT, int f>
 __device__ __forceinline__ float qfeat_val(const float (&x)[D]) {
@@ -285,8 +285,6 @@ __device__ __forceinline__ float qfeat_val(const float (&x)[D]) {
       // product after value numbering
       float p = x[e.idx[0]];
       static_for<1, e.m>([&](auto jj) { p = p * x[e.idx[decltype(jj)::value]]; });
-      constexpr double r = static_cast<double>(e.mult) / static_cast<double>(factorial(e.m));
-      if constexpr (r != 1.0) p = p * static_cast<float>(r);
       return p;
     }
   }
@@ -417,11 +415,13 @@ __device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
   t.kb = b * Cfg::TPK;
   t.kc = c * Cfg::TPK;
   // three-entry bases: key side w u(KS k), query side w alpha_m / KS^m;
-  // otherwise key side u(KS k), query side w^2 alpha_m / KS^m
+  // per-token query features (their own generator): key side
+  // (w^2 / m!) u(KS k); otherwise key side u(KS k), query side
+  // w^2 alpha_m / KS^m
   float cq = (Cfg::TRIPLE ? w : w * w) * inv_mfact;
   for (int j = 0; j < m; ++j) cq *= inv_a / Cfg::KS;
   t.cq = cq;
-  t.ck = Cfg::TRIPLE ? w : 1.f;
+  t.ck = Cfg::TRIPLE ? w : (Cfg::QGEN ? w * w * inv_mfact : 1.f);
   return t;
 }
 
@@ -443,8 +443,10 @@ __device__ __forceinline__ float state_scale(int f) {
     for (int j = 0; j < m; ++j) sc *= 1.f / Cfg::KS;
     return sc;
   } else {
+    // internal rows carry KS^m (and with per-token query features w^2 / m!):
+    // canonical = w / KS^m internal (m! / (w KS^m) internal)
     const PackedFeature e = g_ptab<Cfg::D, Cfg::NT>.e[f];
-    float sc = e.w;
+    float sc = Cfg::QGEN ? 1.f / (e.w * e.inv_mfact) : e.w;
     for (int j = 0; j < static_cast<int>(e.m); ++j) sc *= 1.f / Cfg::KS;
     return sc;
   }
@@ -560,6 +562,7 @@ __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, cons
       for (int t0 = 0; t0 < C; t0 += 8) {
         f16x8 v = *reinterpret_cast<const f16x8*>(ta + t0) * *reinterpret_cast<const f16x8*>(tb + t0);
         if constexpr (Cfg::TRIPLE) v = v * (*reinterpret_cast<const f16x8*>(tc + t0) * ck);
+        if constexpr (Cfg::QGEN) v = v * ck;
         *reinterpret_cast<f16x8*>(dst + fl * Cfg::PK + t0) = v;
       }
     } else {
