@@ -28,6 +28,7 @@
 //    writes o itself; with several slices each writes a partial
 //    (numerator, denominator) and a small kernel sums and divides.
 #include "features.hpp"
+#include "qarrange.hpp"
 #include "internal.hpp"
 #include "mma.hpp"
 
@@ -265,40 +266,62 @@ __device__ __forceinline__ void gen_unrolled(int w, const float (&x)[Cfg::D], ty
 // ---------------------------------------------------------------------------
 // query features per token with compile-time indices (order 4, d = 16)
 // ---------------------------------------------------------------------------
-// Lane t < 32 of a wave generates the query features of token t of the
-// chunk for the wave's FS / NW features of the slice, from its coordinates
-// q / (a KS) held in registers, and stores them as 8-feature packs into the
-// token's row of phi~(Q). The query features are plain products; the key
-// side (table path) carries the weight w^2 / m! = 1 / prod_i c_i! (c_i the
-// multiplicities of the tuple), one packed multiply per eight keys.
+// Features sit in the internal order of qarrange.hpp: per wave range of FW
+// positions, HALF = FW / 2 representatives, then their images under the
+// rotation of the coordinates by d/2. Lane t < 32 of a wave computes the
+// representatives for token t of the chunk from q / (a KS) in registers,
+// lane 32 + t the same instructions on the rotated coordinates, i.e. the
+// images; each stores 16-byte packs into the token's row of phi~(Q). Code is
+// straight-line with compile-time feature indices, one path per slice and
+// wave. The query features are plain products; the key side (table path)
+// carries the weight w^2 / m! = 1 / prod_i c_i! (c_i the multiplicities of
+// the tuple), one packed multiply per eight keys.
+
+template <class Cfg>
+inline constexpr auto kQArr = make_qarrange<Cfg::D, Cfg::NT, Cfg::FS / Cfg::NW / 2>();
+template <class Cfg>
+__device__ const auto g_qarr = kQArr<Cfg>;
+
+// Canonical feature of slice position f (-1: no feature there).
+template <class Cfg>
+__device__ __forceinline__ int canon_feat(int f) {
+  if constexpr (Cfg::QGEN) {
+    return f < kQArr<Cfg>.npos ? g_qarr<Cfg>.perm[f] : -1;
+  } else {
+    return f < Cfg::F ? f : -1;
+  }
+}
 
 template <int D, int NT, int f>
 __device__ __forceinline__ float qfeat_val(const float (&x)[D]) {
-  if constexpr (f >= feature_count(D, NT)) {
-    return 0.f;
+  constexpr Monomial e = kBasis<D, NT>.e[f];
+  if constexpr (e.m == 0) {
+    return 1.f;
   } else {
-    constexpr Monomial e = kBasis<D, NT>.e[f];
-    if constexpr (e.m == 0) {
-      return 1.f;
-    } else {
-      // left-to-right products: features that share a prefix share its
-      // product after value numbering
-      float p = x[e.idx[0]];
-      static_for<1, e.m>([&](auto jj) { p = p * x[e.idx[decltype(jj)::value]]; });
-      return p;
-    }
+    // left-to-right products: features that share a prefix share its
+    // product after value numbering
+    float p = x[e.idx[0]];
+    static_for<1, e.m>([&](auto jj) { p = p * x[e.idx[decltype(jj)::value]]; });
+    return p;
   }
 }
 
 template <class Cfg, int SL, int W>
-__device__ __forceinline__ void gen_q_wave(const float (&x)[Cfg::D], typename Cfg::E* dq) {
-  constexpr int FW = Cfg::FS / Cfg::NW;
-  static_for<0, FW / 8>([&](auto pi) {
+__device__ __forceinline__ void gen_q_wave(const float (&x)[Cfg::D], bool rot, typename Cfg::E* dq) {
+  constexpr int HALF = Cfg::FS / Cfg::NW / 2;
+  static_for<0, HALF / 8>([&](auto pi) {
     constexpr int p = decltype(pi)::value;
     bf16x8 pk;
     static_for<0, 8>([&](auto ji) {
       constexpr int j = decltype(ji)::value;
-      pk[j] = static_cast<__bf16>(qfeat_val<Cfg::D, Cfg::NT, SL * Cfg::FS + W * FW + 8 * p + j>(x));
+      constexpr int i = (SL * Cfg::NW + W) * HALF + 8 * p + j;  // representative
+      float v = 0.f;
+      if constexpr (i < kQArr<Cfg>.nA) {
+        v = qfeat_val<Cfg::D, Cfg::NT, kQArr<Cfg>.a[i]>(x);
+        // a fixed point has no image: the rotated lanes store zero
+        if constexpr (!kQArr<Cfg>.paired[i]) v = rot ? 0.f : v;
+      }
+      pk[j] = static_cast<__bf16>(v);
     });
     *reinterpret_cast<bf16x8*>(dq + 8 * p) = pk;
   });
@@ -310,18 +333,28 @@ template <class Cfg>
 __device__ __forceinline__ void gen_q_token(int gsl, int w, int lane, const typename Cfg::E* sQ,
                                             typename Cfg::E* sPQ, float inv_a) {
   constexpr int D = Cfg::D, FW = Cfg::FS / Cfg::NW;
-  if (lane >= Cfg::C) return;
-  const typename Cfg::E* xr = sQ + lane * Cfg::XP;
+  static_assert(Cfg::C == 32 && D == 16 && Cfg::ES == 2, "one token per lane pair, two 16-byte halves per row");
+  static_assert(kQArr<Cfg>.npos <= Cfg::G * Cfg::FS, "internal order fits the slices");
+  const int t = lane & 31;
+  const bool rot = lane >= 32;
+  // rotation by d/2: the rotated lanes read the two halves of the row swapped
+  const typename Cfg::E* xr = sQ + t * Cfg::XP;
+  const bf16x8 h0 = *reinterpret_cast<const bf16x8*>(xr + (rot ? 8 : 0));
+  const bf16x8 h1 = *reinterpret_cast<const bf16x8*>(xr + (rot ? 0 : 8));
   const float sc = inv_a / Cfg::KS;
   float x[D];
 #pragma unroll
-  for (int j = 0; j < D; ++j) x[j] = static_cast<float>(xr[j]) * sc;
+  for (int j = 0; j < 8; ++j) {
+    x[j] = static_cast<float>(h0[j]) * sc;
+    x[8 + j] = static_cast<float>(h1[j]) * sc;
+  }
+  typename Cfg::E* row = sPQ + t * Cfg::PQ + (rot ? FW / 2 : 0);
   static_for<0, Cfg::G>([&](auto si) {
     constexpr int SL = decltype(si)::value;
     if (gsl == SL) {
       static_for<0, Cfg::NW>([&](auto wi) {
         constexpr int W = decltype(wi)::value;
-        if (w == W) gen_q_wave<Cfg, SL, W>(x, sPQ + lane * Cfg::PQ + W * FW);
+        if (w == W) gen_q_wave<Cfg, SL, W>(x, rot, row + W * FW);
       });
     }
   });
@@ -366,7 +399,8 @@ template <class Cfg>
 __device__ __forceinline__ TabFeat tab_feat(int f, float inv_a) {
   constexpr int D = Cfg::D, TP = Cfg::TP;
   TabFeat t{0, 0, 0, 0, 0, 0, 0.f, 0.f};
-  if (f >= Cfg::F) return t;
+  f = canon_feat<Cfg>(f);  // slice position -> canonical feature
+  if (f < 0) return t;
   int m, i0, i1, i2, i3, i4 = 0, i5 = 0;
   float w, inv_mfact;
   if constexpr (Cfg::TRIPLE) {
@@ -748,9 +782,9 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         for (int ft = 0; ft < FTG; ++ft)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 16 * (ftg0 + ft) + 4 * g4 + i;
+            const int f = canon_feat<Cfg>(f0 + 16 * (ftg0 + ft) + 4 * g4 + i);
             float val = 0.f;
-            if (f < Cfg::F) {
+            if (f >= 0) {
               if (Cfg::ZS || w < NW - 1)
                 val = a.S0[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * (vt0 + j) + c];
               else if (c == 0)
@@ -764,8 +798,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         for (int jz = 0; jz < ZT; ++jz)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 16 * (zlo + jz) + 4 * g4 + i;
-            Z[jz][i] = (c == 0 && jz < nzt && f < Cfg::F)
+            const int f = canon_feat<Cfg>(f0 + 16 * (zlo + jz) + 4 * g4 + i);
+            Z[jz][i] = (c == 0 && jz < nzt && f >= 0)
                            ? a.z0[static_cast<size_t>(bh) * Cfg::F + f] / state_scale<Cfg>(f)
                            : 0.f;
           }
@@ -1288,8 +1322,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         for (int ft = 0; ft < FTG; ++ft)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 16 * (ftg0 + ft) + 4 * g4 + i;
-            if (f < Cfg::F) {
+            const int f = canon_feat<Cfg>(f0 + 16 * (ftg0 + ft) + 4 * g4 + i);
+            if (f >= 0) {
               const float sc = state_scale<Cfg>(f);
               if (Cfg::ZS || w < NW - 1)
                 a.S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * (vt0 + j) + c] = sc * S[j][ft][i];
@@ -1302,8 +1336,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         for (int jz = 0; jz < ZT; ++jz)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int f = f0 + 16 * (zlo + jz) + 4 * g4 + i;
-            if (c == 0 && jz < nzt && f < Cfg::F)
+            const int f = canon_feat<Cfg>(f0 + 16 * (zlo + jz) + 4 * g4 + i);
+            if (c == 0 && jz < nzt && f >= 0)
               a.z[static_cast<size_t>(bh) * Cfg::F + f] = state_scale<Cfg>(f) * Z[jz][i];
           }
       }
@@ -1368,8 +1402,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void state_store_kernel(const float* fin
     for (int ft = 0; ft < FTG; ++ft) {
       const f32x4 val = src[(j * FTG + ft) * 64];
       for (int i = 0; i < 4; ++i) {
-        const int f = gsl * Cfg::FS + 16 * (ftg0 + ft) + 4 * g4 + i;
-        if (f < Cfg::F) {
+        const int f = canon_feat<Cfg>(gsl * Cfg::FS + 16 * (ftg0 + ft) + 4 * g4 + i);
+        if (f >= 0) {
           const float sc = state_scale<Cfg>(f);
           if (Cfg::ZS || w < NW - 1)
             S[(static_cast<size_t>(bh) * Cfg::F + f) * DV + 16 * (vt0 + j) + c] = sc * val[i];
@@ -1384,8 +1418,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void state_store_kernel(const float* fin
     for (int jz = 0; jz < nzt; ++jz) {
       const f32x4 val = src[(NDT * FTG + jz) * 64];
       for (int i = 0; i < 4; ++i) {
-        const int f = gsl * Cfg::FS + 16 * (zlo + jz) + 4 * g4 + i;
-        if (c == 0 && f < Cfg::F) z[static_cast<size_t>(bh) * Cfg::F + f] = state_scale<Cfg>(f) * val[i];
+        const int f = canon_feat<Cfg>(gsl * Cfg::FS + 16 * (zlo + jz) + 4 * g4 + i);
+        if (c == 0 && f >= 0) z[static_cast<size_t>(bh) * Cfg::F + f] = state_scale<Cfg>(f) * val[i];
       }
     }
   }
