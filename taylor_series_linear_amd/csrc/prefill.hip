@@ -1514,27 +1514,27 @@ static void plan_cfg(int BH, int N, PrefillPlan* p) {
     p->L = N;
     return;
   }
-  // eight-wave workgroups (split z) run one per compute unit
-  const int64_t target = Cfg::ZS ? 256 : 512;
-  const int64_t want = (target + static_cast<int64_t>(BH) * Cfg::G - 1) / (static_cast<int64_t>(BH) * Cfg::G);
+  // Eight-wave workgroups (split z) run one per compute unit, the others
+  // two. An update-only chunk of the prefix pass costs about 0.6 of a
+  // read-out chunk (measured for order 4), one of the segment-sum launch
+  // about 0.45, and reading one earlier segment's staged sum about 0.4.
+  const int64_t slots = Cfg::ZS ? 256 : 512;
   const int64_t maxp = nchunks / 4 > 1 ? nchunks / 4 : 1;
-  int64_t P = want < 1 ? 1 : (want > maxp ? maxp : want);
   const int64_t minp = min_segments(nchunks, C, static_cast<int64_t>(Cfg::D > Cfg::DV ? Cfg::D : Cfg::DV) * Cfg::ES);
-  if (P < minp) P = minp;
-  const int64_t cps = (nchunks + P - 1) / P;
-  p->L = static_cast<int>(cps * C);
-  p->P = static_cast<int>((nchunks + cps - 1) / cps);
-  if (p->P == 2 && minp <= 1) {
-    // Two segments: no segment-sum launch; the workgroup of segment 1 first
-    // runs the keys of segment 0 without read-out (measured at about 0.6 of
-    // a read-out chunk for order 4), so segment 0 takes the larger share,
-    // L0 ~ N / (2 - RHO), and both workgroups finish together.
-    constexpr double RHO = 0.6;
-    int64_t c0 = static_cast<int64_t>(static_cast<double>(nchunks) / (2.0 - RHO) + 0.5);
+  const SegChoice sc = choose_segments(static_cast<int64_t>(BH) * Cfg::G, nchunks, slots, minp, maxp, 0.6, 0.45, 0.4);
+  if (sc.prefix) {
+    // segment 0 takes the larger share, L0 ~ N / (2 - 0.6), so that both
+    // workgroups of a (head, slice) finish together
+    int64_t c0 = static_cast<int64_t>(static_cast<double>(nchunks) / (2.0 - 0.6) + 0.5);
     if (c0 > nchunks - 1) c0 = nchunks - 1;
     if (c0 < 1) c0 = 1;
+    p->P = 2;
     p->L0 = static_cast<int>(c0 * C);
     p->L = p->L0;
+  } else {
+    const int64_t cps = (nchunks + sc.P - 1) / sc.P;
+    p->L = static_cast<int>(cps * C);
+    p->P = static_cast<int>((nchunks + cps - 1) / cps);
   }
   // staged states: G slices x SLICE_F4 float4s per (head, segment)
   const size_t UB = static_cast<size_t>(Cfg::G) * Cfg::SLICE_F4 * 16;

@@ -45,6 +45,49 @@ TL_HD inline Split split_segments(int BH, int64_t N, int chunk, int64_t target, 
   return Split{static_cast<int>((nch + cps - 1) / cps), static_cast<int>(cps * chunk)};
 }
 
+// Segments per head for the generic prefill kernels: the P that minimises
+// an estimate of the call's time in units of one read-out chunk on one
+// workgroup slot. `units` workgroups run per segment (heads x feature
+// slices), `slots` are resident at once. P = 1: one round of
+// ceil(units / slots) over all chunks. P = 2 with a prefix pass (segment 1
+// first runs segment 0's keys without read-out, at rho_pre of a read-out
+// chunk each): segment 0 takes nchunks / (2 - rho_pre) chunks and sets the
+// time. P >= 2 with segment sums: a sum launch over P - 1 segments (rho_sum
+// per chunk) then the main launch over P, each in ceil(workgroups / slots)
+// rounds of ceil(nchunks / P) chunks, a main-launch workgroup also reading up
+// to P - 1 earlier sums (rho_read each). Ties keep the smaller P; P stays
+// within [minp, maxp] and the prefix pass needs minp == 1 (all rows of the
+// head in one 32-bit buffer range).
+struct SegChoice {
+  int P;
+  bool prefix;  // two segments with a prefix pass (no segment sums)
+};
+TL_HD inline SegChoice choose_segments(int64_t units, int64_t nchunks, int64_t slots, int64_t minp, int64_t maxp,
+                                       double rho_pre, double rho_sum, double rho_read) {
+  auto rounds = [&](int64_t w) { return static_cast<double>((w + slots - 1) / slots); };
+  if (maxp < minp) maxp = minp;
+  SegChoice best{static_cast<int>(minp), false};
+  double best_cost = 1e300;
+  for (int64_t P = minp; P <= maxp && P <= 256; ++P) {
+    const double cps = static_cast<double>((nchunks + P - 1) / P);
+    double cost;
+    bool prefix = false;
+    if (P == 1) {
+      cost = rounds(units) * static_cast<double>(nchunks);
+    } else if (P == 2 && minp <= 1) {
+      cost = rounds(2 * units) * static_cast<double>(nchunks) / (2.0 - rho_pre);
+      prefix = true;
+    } else {
+      cost = rounds(units * P) * (cps + static_cast<double>(P - 1) * rho_read) + rounds(units * (P - 1)) * cps * rho_sum;
+    }
+    if (cost < best_cost * (1.0 - 1e-9)) {
+      best_cost = cost;
+      best = SegChoice{static_cast<int>(P), prefix};
+    }
+  }
+  return best;
+}
+
 namespace o2s {
 
 // Workgroups of the single-pass order-2 kernel are dispatched to the 8 XCDs
