@@ -49,7 +49,8 @@ PREFILLS = {
                                 bound="mfma", replicas=2),
     "based_order2_prefill": dict(sources=("prefill_o2.hip", "internal.hpp", "mma.hpp", "sched.hpp"),
                                  bound="hbm", replicas=4),
-    "order4_prefill": dict(sources=("prefill.hip", "features.hpp", "internal.hpp", "mma.hpp", "sched.hpp"),
+    "order4_prefill": dict(sources=("prefill.hip", "features.hpp", "qarrange.hpp", "rank.hpp", "internal.hpp",
+                                    "mma.hpp", "sched.hpp"),
                            bound="mfma", replicas=8),
 }
 
