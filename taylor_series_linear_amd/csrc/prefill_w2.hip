@@ -377,15 +377,19 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     const int r = c * C + row;
     return static_cast<uint32_t>(r < static_cast<int>(seg_rows) ? r : static_cast<int>(seg_rows));
   };
-  // item of this thread: threads 0..255 a Q item, 256..511 a K item (row
-  // it >> 3, coordinates 8 (it & 7) .. +8); threads 0..127 also a V item
-  // (row tid >> 2, this half's columns 8 (tid & 3) .. +8). Rows past the
-  // segment's end load as zero (buffer range), so they add nothing.
+  // item of this thread: threads 0..255 a Q item (row it >> 3, coordinates
+  // 8 (it & 7) .. +8), 256..511 a K item; threads 0..127 also a V item (this
+  // half's columns 8 vc4 .. +8). K and V are written transposed, 2 bytes per
+  // element: their items put the 32 rows of a chunk on the lanes of each half
+  // wave (row it & 31, coordinates 8 (2 (it >> 6) + bit 5 of it), columns 8
+  // (tid >> 5)), so a wave's stores spread over 32 banks (with eight rows per
+  // wave four lanes shared a bank; the call is 1.4% faster this way). Rows
+  // past the segment's end load as zero (buffer range), so they add nothing.
   const bool is_q = __builtin_amdgcn_readfirstlane(tid) < 256;
   const int it = is_q ? tid : tid - 256;
-  const int irow = it >> 3, ic8 = it & 7;
+  const int irow = is_q ? it >> 3 : (it & 31), ic8 = is_q ? it & 7 : 2 * (it >> 6) + ((it >> 5) & 1);
   const bool has_v = tid < 128;
-  const int vrow = tid >> 2, vc4 = tid & 3;
+  const int vrow = tid & 31, vc4 = tid >> 5;
   auto load_a = [&](int c) __attribute__((always_inline)) -> uint4 {
     return bload16(is_q ? rq : rk, (crow(c, irow) * D + 8 * ic8) * 2);
   };
