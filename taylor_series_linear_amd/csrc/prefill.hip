@@ -146,11 +146,11 @@ struct PCfg {
   static constexpr int OFF_TQ = OFF_DEN + (ZS_() ? NW : 1) * C * 4;
   static constexpr int OFF_TK = OFF_TQ + TQE * TP * 4;
   static constexpr int TAB_END = OFF_TK + TE * TPK * KES;
-  // split z: the read-out partials of feature groups 1 .. NFG-1 ([NFG-1][C]
-  // [DV], f32x4 per lane and tile) reuse the factor tables, which are dead
-  // from the feature generation to the next chunk's staging
+  // split z: the read-out partials of the NFG feature groups ([NFG][C][DV],
+  // f32x4 per lane and tile) reuse the factor tables, which are dead from the
+  // feature generation to the next chunk's staging
   static constexpr int OFF_RED = OFF_TQ;
-  static constexpr int RED_END = OFF_RED + (ZS_() ? (NFG - 1) * C * DV * 4 : 0);
+  static constexpr int RED_END = OFF_RED + (ZS_() ? NFG * C * DV * 4 : 0);
   static constexpr int LDS = TAB_END > RED_END ? TAB_END : RED_END;
   static_assert(NT <= 7, "features are products of at most three table entries (order 6)");
   static_assert(!TRIPLE || (PAIRS && !UNROLL), "orders 5 and 6 use the table-driven generator with pairs");
@@ -159,6 +159,7 @@ struct PCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(DV + NDEN <= PPITCH, "partial-output row holds the values and the denominator columns");
   static_assert(!ZS || (FS % (32 * NFG) == 0 && DV == 16 * NDT * (NW / NFG)), "split z: whole k-steps per group");
+  static_assert(!ZS || (C / 16) * (DV / 16) * 64 == NTHR, "split z: one output item of the chunk per thread");
   static_assert(!QGEN || (ZS && FS % (8 * NW) == 0), "per-token generator: whole 8-feature packs per wave");
   // score tiles (kt, qt) needed per chunk: key tiles up to the end of the
   // 32-key step that contains the diagonal tile
@@ -564,23 +565,43 @@ __device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, fl
   }
 }
 
+// Blocks of 64 features of the table-driven generators, per wave: entry j
+// of wave w is block w + NW j, except that when the blocks beyond one per
+// wave (R of them, fewer than the waves) divide the waves, each of them is
+// split by tokens over NW / R waves, so that every wave does the same work
+// (a 640-feature slice on eight waves: one block and a quarter of one).
+template <class Cfg>
+struct TabSplit {
+  static constexpr int NB = (Cfg::FS + 63) / 64, NW = Cfg::NW, R = NB - NW;
+  static constexpr bool BAL = R > 0 && R < NW && NW % R == 0 && (Cfg::C / (NW / R)) % 8 == 0;
+  static constexpr int P = BAL ? NW / R : 1;     // token pieces per left-over block
+  static constexpr int NBW = (NB + NW - 1) / NW;  // entries per wave
+  __device__ static int block(int w, int j) { return BAL ? (j == 0 ? w : NW + w / P) : w + NW * j; }
+  __device__ static int tok0(int w, int j) { return BAL && j > 0 ? (w % P) * (Cfg::C / P) : 0; }
+  template <int J>
+  static constexpr int ntok() { return BAL && J > 0 ? Cfg::C / P : Cfg::C; }
+};
+
 // Query side: phi~(Q) [C x FS], query-major. Key side: u(KS K)^T [FS x C].
 template <class Cfg, bool QSIDE, class TE_, class DE>
 __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, const TE_* __restrict__ T,
                                         DE* __restrict__ dst) {
-  constexpr int NB = (Cfg::FS + 63) / 64, NBW = (NB + Cfg::NW - 1) / Cfg::NW, C = Cfg::C;
-#pragma unroll
-  for (int j = 0; j < NBW; ++j) {
-    const int blk = w + Cfg::NW * j;
+  using TS = TabSplit<Cfg>;
+  static_for<0, TS::NBW>([&](auto ji) {
+    constexpr int j = decltype(ji)::value;
+    constexpr int NTOK = TS::template ntok<j>();
+    const int blk = TS::block(w, j);
     const int fl = 64 * blk + lane;
-    if (blk >= NB || fl >= Cfg::FS) continue;
+    if (blk >= TS::NB || fl >= Cfg::FS) return;
+    const int tbase = TS::tok0(w, j);
     if constexpr (QSIDE) {
       const float* __restrict__ ta = T + tf[j].oa;
       const float* __restrict__ tb = T + tf[j].ob;
       const float* __restrict__ tc = T + tf[j].oc;
       const float cf = tf[j].cq;
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 4) {
+      for (int tt = 0; tt < NTOK; tt += 4) {
+        const int t0 = tbase + tt;
         const f32x4 va = *reinterpret_cast<const f32x4*>(ta + t0);
         f32x4 vb = *reinterpret_cast<const f32x4*>(tb + t0);
         if constexpr (Cfg::TRIPLE) vb *= *reinterpret_cast<const f32x4*>(tc + t0);
@@ -593,7 +614,8 @@ __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, cons
       const TE_* tc = T + tf[j].kc;
       const _Float16 ck = static_cast<_Float16>(tf[j].ck);
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 8) {
+      for (int tt = 0; tt < NTOK; tt += 8) {
+        const int t0 = tbase + tt;
         f16x8 v = *reinterpret_cast<const f16x8*>(ta + t0) * *reinterpret_cast<const f16x8*>(tb + t0);
         if constexpr (Cfg::TRIPLE) v = v * (*reinterpret_cast<const f16x8*>(tc + t0) * ck);
         if constexpr (Cfg::QGEN) v = v * ck;
@@ -605,13 +627,14 @@ __device__ __forceinline__ void gen_tab(int w, int lane, const TabFeat* tf, cons
       const TE_* tc = T + tf[j].kc;
       const float ck = tf[j].ck;
 #pragma unroll
-      for (int t0 = 0; t0 < C; t0 += 4) {
+      for (int tt = 0; tt < NTOK; tt += 4) {
+        const int t0 = tbase + tt;
         f32x4 v = *reinterpret_cast<const f32x4*>(ta + t0) * *reinterpret_cast<const f32x4*>(tb + t0);
         if constexpr (Cfg::TRIPLE) v = v * (*reinterpret_cast<const f32x4*>(tc + t0) * ck);
         *reinterpret_cast<f32x4*>(dst + fl * Cfg::PK + t0) = v;
       }
     }
-  }
+  });
 }
 
 // Score tiles of one chunk handled by wave R (tiles R, R+NW, ...): all
@@ -848,14 +871,14 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   const float inv_a = a.inv_a;
 
   // table-driven generator: this lane's features (fixed for the kernel)
-  constexpr int NBW = ((Cfg::FS + 63) / 64 + NW - 1) / NW;
+  constexpr int NBW = TabSplit<Cfg>::NBW;
   TabFeat tf[NBW];
   float* sTQ = reinterpret_cast<float*>(smem + Cfg::OFF_TQ);
   KE* sTK = reinterpret_cast<KE*>(smem + Cfg::OFF_TK);
   const PairJobs<Cfg> pj = pair_jobs<Cfg>(tid);
   if constexpr (Cfg::TAB) {
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) tf[j] = tab_feat<Cfg>(f0 + 64 * (w + NW * j) + lane, inv_a);
+    for (int j = 0; j < NBW; ++j) tf[j] = tab_feat<Cfg>(f0 + 64 * TabSplit<Cfg>::block(w, j) + lane, inv_a);
     // row 0 of both tables is the constant 1 (also for rows past the end of
     // the sequence: their values and ones-row entries are zero)
     for (int t = tid; t < Cfg::C; t += Cfg::NTHR) {
@@ -1123,31 +1146,45 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         });
       }
       if constexpr (Cfg::ZS) {
-        // feature groups 1 .. NFG-1 hand their value partials to group 0,
-        // every wave its share of the denominator
-        if (fg > 0) {
+        // every feature group hands its value partials, every wave its
+        // share of the denominator, to LDS; then each thread sums one output
+        // item of the chunk (query tile iqt, value tile ivt, accumulator lane
+        // il: four values of one query), so that the sums, the normalisation
+        // and the stores are spread over all waves
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt)
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-            for (int j = 0; j < NDT; ++j)
-              sRed[(((fg - 1) * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane] = acc[j][qt];
-        }
+          for (int j = 0; j < NDT; ++j) sRed[((fg * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane] = acc[j][qt];
         if (g4 == 0) {
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) sDen[w * C + 16 * qt + c] = accZ[qt][0];
         }
         __syncthreads();
-        if (fg == 0) {
+        const int il = tid & 63, ivt = (tid >> 6) % (DV / 16), iqt = tid / (64 * (DV / 16));
+        f32x4 o = sRed[(iqt * (DV / 16) + ivt) * 64 + il];
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
+        for (int g = 1; g < Cfg::NFG; ++g) o += sRed[((g * QT + iqt) * (DV / 16) + ivt) * 64 + il];
+        const int qi = 16 * iqt + (il & 15), col = 16 * ivt + 4 * (il >> 4);
+        float dsum = 0.f;
 #pragma unroll
-            for (int g = 0; g < Cfg::NFG - 1; ++g)
+        for (int ww = 0; ww < NW; ++ww) dsum += sDen[ww * C + qi];
+        if (qi < nv) {
+          if constexpr (G == 1) {
+            const float r = 1.f / dsum;
+            const size_t off = (static_cast<size_t>(bh) * N + c0 + qi) * DV + col;
+            if (a.out_bf16) {
+              bf16x4 ov;
 #pragma unroll
-              for (int j = 0; j < NDT; ++j) acc[j][qt] += sRed[((g * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane];
-            float dsum = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) dsum += sDen[ww * C + 16 * qt + c];
-            accZ[qt][0] = dsum;
+              for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(o[i] * r);
+              *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
+            } else {
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = o * r;
+            }
+          } else {
+            // partial row: the values, and the denominator in column DV
+            float* pr = a.part + ((static_cast<size_t>(gsl) * a.BH + bh) * N + c0 + qi) * Cfg::PPITCH;
+            *reinterpret_cast<f32x4*>(pr + col) = o;
+            if (col == 0) pr[DV] = dsum;
           }
         }
       } else if constexpr (G == 1) {
@@ -1162,7 +1199,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           for (int qt = 0; qt < QT; ++qt) accZ[qt][0] = sDen[16 * qt + c];
         }
       }
-      if (Cfg::ZS ? fg == 0 : (w < NW - 1 || G > 1)) {
+      if (!Cfg::ZS && (w < NW - 1 || G > 1)) {
         if constexpr (G == 1) {
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) {
@@ -1190,13 +1227,12 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           for (int qt = 0; qt < QT; ++qt) {
             const int qi = 16 * qt + c;
             if (qi < nv) {
-              if (Cfg::ZS || w < NW - 1) {
+              if (w < NW - 1) {
 #pragma unroll
                 for (int j = 0; j < NDT; ++j)
                   *reinterpret_cast<f32x4*>(pp + qi * Cfg::PPITCH + 16 * (vt0 + j) + 4 * g4) = acc[j][qt];
               }
-              if (Cfg::ZS ? (w == 0 && g4 == 0) : (w == NW - 1 && g4 == 0))
-                pp[qi * Cfg::PPITCH + DV] = Cfg::ZS ? accZ[qt][0] : acc[0][qt][0];
+              if (w == NW - 1 && g4 == 0) pp[qi * Cfg::PPITCH + DV] = acc[0][qt][0];
             }
           }
         }
