@@ -84,6 +84,11 @@ struct PCfg {
   // two or three MFMAs. Otherwise one wave per value tile holds all of the
   // slice's features and a last wave holds z as a sixteen-column tile.
   static constexpr bool ZS = ZS_();
+  // wide split-z slices (one workgroup per compute unit in any case): the
+  // read-out partials of every feature group go through LDS and all waves
+  // sum, normalise and store the chunk's output; narrower ones keep to the
+  // LDS budget of two workgroups per compute unit (group 0 sums)
+  static constexpr bool WIDE = ZS && FS >= 512;
   static constexpr int NDT = ZS ? 2 : 1;  // value tiles per wave
   static constexpr int NFG = ZS ? 4 : 1;  // feature groups
   static constexpr int NW = ZS ? (DV / 16 / NDT) * NFG : DV / 16 + 1;
@@ -107,7 +112,9 @@ struct PCfg {
   static constexpr int PADE = 16 / ES; // 16 bytes of padding, in elements
   static constexpr int XP = D + PADE;  // Q/K tile pitch
   static constexpr int PQ = FS + PADE; // phi~(Q) pitch (query-major)
-  static constexpr int PK = C + PADE;  // phi(K)^T, V^T pitch (key-contiguous)
+  // phi(K)^T, V^T pitch (key-contiguous); wide bf16 slices pad by 48 bytes
+  // (order 4: 1.2% faster than 16, same bank-conflict count)
+  static constexpr int PK = C + (WIDE && ES == 2 ? 24 : PADE);
   static constexpr int PP = C + PADE;  // P^T pitch (query-major, keys contiguous)
   static constexpr int PPITCH = DV + 4;  // partial-output row pitch (floats)
   // LDS layout (bytes)
@@ -146,11 +153,12 @@ struct PCfg {
   static constexpr int OFF_TQ = OFF_DEN + (ZS_() ? NW : 1) * C * 4;
   static constexpr int OFF_TK = OFF_TQ + TQE * TP * 4;
   static constexpr int TAB_END = OFF_TK + TE * TPK * KES;
-  // split z: the read-out partials of the NFG feature groups ([NFG][C][DV],
-  // f32x4 per lane and tile) reuse the factor tables, which are dead from the
-  // feature generation to the next chunk's staging
+  // split z: the read-out partials of the feature groups (all of them, or
+  // 1 .. NFG-1 when group 0 sums; [C][DV] each, f32x4 per lane and tile)
+  // reuse the factor tables, which are dead from the feature generation to
+  // the next chunk's staging
   static constexpr int OFF_RED = OFF_TQ;
-  static constexpr int RED_END = OFF_RED + (ZS_() ? NFG * C * DV * 4 : 0);
+  static constexpr int RED_END = OFF_RED + (ZS_() ? (WIDE ? NFG : NFG - 1) * C * DV * 4 : 0);
   static constexpr int LDS = TAB_END > RED_END ? TAB_END : RED_END;
   static_assert(NT <= 7, "features are products of at most three table entries (order 6)");
   static_assert(!TRIPLE || (PAIRS && !UNROLL), "orders 5 and 6 use the table-driven generator with pairs");
@@ -159,7 +167,7 @@ struct PCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(DV + NDEN <= PPITCH, "partial-output row holds the values and the denominator columns");
   static_assert(!ZS || (FS % (32 * NFG) == 0 && DV == 16 * NDT * (NW / NFG)), "split z: whole k-steps per group");
-  static_assert(!ZS || (C / 16) * (DV / 16) * 64 == NTHR, "split z: one output item of the chunk per thread");
+  static_assert(!WIDE || (C / 16) * (DV / 16) * 64 == NTHR, "wide split z: one output item of the chunk per thread");
   static_assert(!QGEN || (ZS && FS % (8 * NW) == 0), "per-token generator: whole 8-feature packs per wave");
   // score tiles (kt, qt) needed per chunk: key tiles up to the end of the
   // 32-key step that contains the diagonal tile
@@ -907,6 +915,15 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   const auto rq = make_rsrc(qh + static_cast<size_t>(t0) * D, want_out ? seg_rows * D * Cfg::ES : 0u);
   const auto rk = make_rsrc(kh + static_cast<size_t>(lo) * D, loop_rows * D * Cfg::ES);
   const auto rv = make_rsrc(vh + static_cast<size_t>(lo) * DV, loop_rows * DV * Cfg::ES);
+  // V items (16 bytes each). V is written transposed, one element per
+  // store: in wide slices consecutive lanes take consecutive rows (tokens)
+  // of one 16-byte column group, so that the stores of a wave spread over
+  // the banks (in the row-major order of a row's items, four different
+  // dwords of a wave's store shared a bank at dv = 64; order 4 runs 1%
+  // faster); the narrower instantiations keep the row-major order, which
+  // coalesces their global loads better
+  auto v_row = [](int j) { return Cfg::WIDE ? j % C : j / (DV / EV); };
+  auto v_col = [](int j) { return Cfg::WIDE ? (j / C) * EV : (j % (DV / EV)) * EV; };
   auto fetch = [&](int cc0) {
     const uint32_t r0 = static_cast<uint32_t>(cc0 - lo);
     const bool qrows = cc0 >= t0;  // prefix-pass chunks read no queries
@@ -923,7 +940,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         pf[s] = bload16(rk, ((r0 + row) * D + col) * Cfg::ES);
       } else if (i < NIT) {
         const int j = i - QB - NQI;
-        const int row = j / (DV / EV), col = (j % (DV / EV)) * EV;
+        const int row = v_row(j), col = v_col(j);
         pf[s] = bload16(rv, ((r0 + row) * DV + col) * Cfg::ES);
       }
     }
@@ -974,7 +991,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         }
       } else if (i < NIT) {
         const int j = i - QB - NQI;
-        const int row = j / (DV / EV), col = (j % (DV / EV)) * EV;
+        const int row = v_row(j), col = v_col(j);
         const E* e = reinterpret_cast<const E*>(&pf[s]);
 #pragma unroll
         for (int u = 0; u < EV; ++u) sV[(col + u) * Cfg::PK + row] = e[u];
@@ -1146,47 +1163,76 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
         });
       }
       if constexpr (Cfg::ZS) {
-        // every feature group hands its value partials, every wave its
-        // share of the denominator, to LDS; then each thread sums one output
-        // item of the chunk (query tile iqt, value tile ivt, accumulator lane
-        // il: four values of one query), so that the sums, the normalisation
-        // and the stores are spread over all waves
+        if constexpr (Cfg::WIDE) {
+          // every feature group hands its value partials, every wave its
+          // share of the denominator, to LDS; then each thread sums one output
+          // item of the chunk (query tile iqt, value tile ivt, accumulator lane
+          // il: four values of one query), so that the sums, the normalisation
+          // and the stores are spread over all waves
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
+          for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-          for (int j = 0; j < NDT; ++j) sRed[((fg * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane] = acc[j][qt];
-        if (g4 == 0) {
+            for (int j = 0; j < NDT; ++j) sRed[((fg * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane] = acc[j][qt];
+          if (g4 == 0) {
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) sDen[w * C + 16 * qt + c] = accZ[qt][0];
-        }
-        __syncthreads();
-        const int il = tid & 63, ivt = (tid >> 6) % (DV / 16), iqt = tid / (64 * (DV / 16));
-        f32x4 o = sRed[(iqt * (DV / 16) + ivt) * 64 + il];
-#pragma unroll
-        for (int g = 1; g < Cfg::NFG; ++g) o += sRed[((g * QT + iqt) * (DV / 16) + ivt) * 64 + il];
-        const int qi = 16 * iqt + (il & 15), col = 16 * ivt + 4 * (il >> 4);
-        float dsum = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) dsum += sDen[ww * C + qi];
-        if (qi < nv) {
-          if constexpr (G == 1) {
-            const float r = 1.f / dsum;
-            const size_t off = (static_cast<size_t>(bh) * N + c0 + qi) * DV + col;
-            if (a.out_bf16) {
-              bf16x4 ov;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(o[i] * r);
-              *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
-            } else {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = o * r;
-            }
-          } else {
-            // partial row: the values, and the denominator in column DV
-            float* pr = a.part + ((static_cast<size_t>(gsl) * a.BH + bh) * N + c0 + qi) * Cfg::PPITCH;
-            *reinterpret_cast<f32x4*>(pr + col) = o;
-            if (col == 0) pr[DV] = dsum;
+            for (int qt = 0; qt < QT; ++qt) sDen[w * C + 16 * qt + c] = accZ[qt][0];
           }
-        }
+          __syncthreads();
+          const int il = tid & 63, ivt = (tid >> 6) % (DV / 16), iqt = tid / (64 * (DV / 16));
+          f32x4 o = sRed[(iqt * (DV / 16) + ivt) * 64 + il];
+#pragma unroll
+          for (int g = 1; g < Cfg::NFG; ++g) o += sRed[((g * QT + iqt) * (DV / 16) + ivt) * 64 + il];
+          const int qi = 16 * iqt + (il & 15), col = 16 * ivt + 4 * (il >> 4);
+          float dsum = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) dsum += sDen[ww * C + qi];
+          if (qi < nv) {
+            if constexpr (G == 1) {
+              const float r = 1.f / dsum;
+              const size_t off = (static_cast<size_t>(bh) * N + c0 + qi) * DV + col;
+              if (a.out_bf16) {
+                bf16x4 ov;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(o[i] * r);
+                *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(a.o) + off) = ov;
+              } else {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + off) = o * r;
+              }
+            } else {
+              // partial row: the values, and the denominator in column DV
+              float* pr = a.part + ((static_cast<size_t>(gsl) * a.BH + bh) * N + c0 + qi) * Cfg::PPITCH;
+              *reinterpret_cast<f32x4*>(pr + col) = o;
+              if (col == 0) pr[DV] = dsum;
+            }
+          }        } else {
+          // feature groups 1 .. NFG-1 hand their value partials to group 0,
+          // every wave its share of the denominator
+          if (fg > 0) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+              for (int j = 0; j < NDT; ++j)
+                sRed[(((fg - 1) * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane] = acc[j][qt];
+          }
+          if (g4 == 0) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) sDen[w * C + 16 * qt + c] = accZ[qt][0];
+          }
+          __syncthreads();
+          if (fg == 0) {
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+              for (int g = 0; g < Cfg::NFG - 1; ++g)
+#pragma unroll
+                for (int j = 0; j < NDT; ++j) acc[j][qt] += sRed[((g * QT + qt) * (DV / 16) + vt0 + j) * 64 + lane];
+              float dsum = 0.f;
+#pragma unroll
+              for (int ww = 0; ww < NW; ++ww) dsum += sDen[ww * C + 16 * qt + c];
+              accZ[qt][0] = dsum;
+            }
+          }        }
+
       } else if constexpr (G == 1) {
         // denominator: row DV of O^T (wave NW-1, lane group 0, element 0)
         if (w == NW - 1 && g4 == 0) {
@@ -1199,7 +1245,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           for (int qt = 0; qt < QT; ++qt) accZ[qt][0] = sDen[16 * qt + c];
         }
       }
-      if (!Cfg::ZS && (w < NW - 1 || G > 1)) {
+      if (Cfg::ZS ? (!Cfg::WIDE && fg == 0) : (w < NW - 1 || G > 1)) {
         if constexpr (G == 1) {
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) {
@@ -1227,12 +1273,13 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
           for (int qt = 0; qt < QT; ++qt) {
             const int qi = 16 * qt + c;
             if (qi < nv) {
-              if (w < NW - 1) {
+              if (Cfg::ZS || w < NW - 1) {
 #pragma unroll
                 for (int j = 0; j < NDT; ++j)
                   *reinterpret_cast<f32x4*>(pp + qi * Cfg::PPITCH + 16 * (vt0 + j) + 4 * g4) = acc[j][qt];
               }
-              if (w == NW - 1 && g4 == 0) pp[qi * Cfg::PPITCH + DV] = acc[0][qt][0];
+              if (Cfg::ZS ? (w == 0 && g4 == 0) : (w == NW - 1 && g4 == 0))
+                pp[qi * Cfg::PPITCH + DV] = Cfg::ZS ? accZ[qt][0] : acc[0][qt][0];
             }
           }
         }
