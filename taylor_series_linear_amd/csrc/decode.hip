@@ -18,6 +18,8 @@
 // weights phi(k), alpha*phi(q) are computed once per head into LDS. State
 // accesses are non-temporal: each byte is touched once per step, and the
 // streaming hint lifts the read-modify-write rate above that of a plain copy.
+#include <type_traits>
+
 #include "features.hpp"
 #include "internal.hpp"
 #include "mma.hpp"
@@ -335,49 +337,93 @@ __global__ __launch_bounds__(1024) void decode_wide_kernel(DecodeArgs a) {
 }
 
 // Feature map, phi[row, f] = w_f * scale[m_f] * prod_j x[row, i_j]. A
-// workgroup covers a block of FM_ROWS rows and FM_FPT * 256 consecutive
-// features: every thread decodes its first feature once and steps through
-// the rest (no per-element index arithmetic or table lookup), the block's
-// input rows are staged in LDS, and each row's outputs are written by
-// consecutive threads, so the stores of a wave cover one contiguous stretch
-// of the output row. The kernel is bound by the HBM write of phi.
+// workgroup covers a block of FM_ROWS rows and FM_FB consecutive features;
+// the block's input rows are staged in LDS. Every thread decodes the seven
+// features around its four (offsets -3 .. +3) once and steps through them
+// (no per-element index arithmetic or table lookup). A row's stretch of
+// outputs starts at an arbitrary 4-byte offset (F is odd), so per row the
+// threads shift their four outputs by the stretch's misalignment s (the
+// same for the whole block): thread t writes elements 4t - s .. 4t - s + 3
+// of the stretch with one 16-byte store at a 16-byte aligned address, and
+// the consecutive stores of a wave cover a contiguous part of the row. Only
+// the first and the last thread of a stretch write single elements. When a
+// row has at most 253 features a wave covers it and the four waves of the
+// workgroup work on four rows at a time; every wave then holds a row's ends,
+// so there each thread writes its four features with 4-byte stores instead
+// (no shift). The kernel is bound by the HBM write of phi.
 constexpr int FM_ROWS = 64;
-constexpr int FM_FPT = 4;  // features per thread
+constexpr int FM_FPT = 4;                       // outputs per thread and row
+constexpr int FM_FB = 256 * FM_FPT - FM_FPT;    // features per block: shifted windows of 1024 cover them
+constexpr int FM_WIN = FM_FPT + 3;              // features a thread holds
 template <int D, int NT, bool BF16>
 __global__ __launch_bounds__(256) void feature_map_kernel(const void* x, int64_t rows, float* phi,
                                                           OrderScale sc) {
   constexpr int F = feature_count(D, NT);
+  constexpr int TPR = F + 3 <= 64 * FM_FPT ? 64 : 256;  // threads per row
+  constexpr int NGR = 256 / TPR;                        // rows at a time
   __shared__ float xs[FM_ROWS * D];
   const int tid = threadIdx.x;
+  const int tr = tid % TPR, grp = tid / TPR;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * FM_ROWS;
   const int nr = static_cast<int>(rows - r0 < FM_ROWS ? rows - r0 : FM_ROWS);
   for (int i = tid; i < nr * D; i += 256) xs[i] = load_in<BF16>(x, static_cast<size_t>(r0) * D + i);
   __syncthreads();
-  const int f0 = (static_cast<int>(blockIdx.y) * 256 + tid) * FM_FPT;
-  if (f0 >= F) return;
-  // this thread's features: coefficient and indices, in registers
-  float cf[FM_FPT];
-  int ix[FM_FPT][kMaxOrderRank];
-  int mm[FM_FPT];
-  RankedFeature e = rank_decode(D, NT, f0);
+  const int fb = static_cast<int>(blockIdx.y) * FM_FB;
+  const int nf = F - fb < FM_FB ? F - fb : FM_FB;  // features of this block
+  // features f0 - 3 .. f0 + 3 of this thread: coefficient (zero outside the
+  // basis) and indices, in registers
+  const int fs = fb + FM_FPT * tr - 3;
+  float cf[FM_WIN];
+  int ix[FM_WIN][kMaxOrderRank];
+  int mm[FM_WIN];
+  RankedFeature e = rank_decode(D, NT, fs < 0 ? 0 : fs);
 #pragma unroll
-  for (int j = 0; j < FM_FPT; ++j) {
-    cf[j] = f0 + j < F ? e.w * sc.s[e.m] : 0.f;
-    mm[j] = e.m;
+  for (int k = 0; k < FM_WIN; ++k) {
+    const int fk = fs + k;
+    cf[k] = fk >= 0 && fk < F ? e.w * sc.s[e.m] : 0.f;
+    mm[k] = e.m;
 #pragma unroll
-    for (int u = 0; u < kMaxOrderRank; ++u) ix[j][u] = e.idx[u];
-    if (j + 1 < FM_FPT) rank_next(D, e);
+    for (int u = 0; u < kMaxOrderRank; ++u) ix[k][u] = e.idx[u];
+    if (k + 1 < FM_WIN && fk >= 0) rank_next(D, e);
   }
-  for (int r = 0; r < nr; ++r) {
+  // phi's own misalignment in elements
+  const int mis = static_cast<int>((reinterpret_cast<uintptr_t>(phi) >> 2) & 3);
+  for (int r = grp; r < nr; r += NGR) {
     const float* xr = xs + r * D;
-    float* dst = phi + (r0 + r) * F + f0;
+    const int64_t g = (r0 + r) * static_cast<int64_t>(F) + fb;  // first element of the row's stretch
+    const int s = TPR == 64 ? 0 : static_cast<int>((g + mis) & 3);
+    const int lo = FM_FPT * tr - s;  // this thread's first element within the stretch
+    if (lo >= nf) continue;
+    auto out = [&](auto stag) __attribute__((always_inline)) {
+      constexpr int S = decltype(stag)::value;
+      f32x4 v;
 #pragma unroll
-    for (int j = 0; j < FM_FPT; ++j) {
-      float v = cf[j];
+      for (int j = 0; j < FM_FPT; ++j) {
+        const int k = j - S + 3;
+        float p = cf[k];
 #pragma unroll
-      for (int u = 0; u < kMaxOrderRank; ++u)
-        if (u < mm[j]) v *= xr[ix[j][u]];
-      if (f0 + j < F) dst[j] = v;
+        for (int u = 0; u < kMaxOrderRank; ++u)
+          if (u < mm[k]) p *= xr[ix[k][u]];
+        v[j] = p;
+      }
+      float* dst = phi + g + lo;
+      if (TPR != 64 && lo >= 0 && lo + FM_FPT <= nf) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int j = 0; j < FM_FPT; ++j)
+          if (lo + j >= 0 && lo + j < nf) dst[j] = v[j];
+      }
+    };
+    if constexpr (TPR == 64) {
+      out(std::integral_constant<int, 0>{});
+    } else {
+      switch (s) {
+        case 0: out(std::integral_constant<int, 0>{}); break;
+        case 1: out(std::integral_constant<int, 1>{}); break;
+        case 2: out(std::integral_constant<int, 2>{}); break;
+        default: out(std::integral_constant<int, 3>{}); break;
+      }
     }
   }
 }
@@ -432,7 +478,7 @@ hipError_t feature_map_launch(int d, int n_terms, bool bf16, const void* x, int6
   if (rb > 0x7fffffff) return hipErrorInvalidValue;
 #define X(D, NT)                                                                                       \
   if (d == D && n_terms == NT) {                                                                       \
-    const dim3 grid(static_cast<unsigned>(rb), (feature_count(D, NT) + 256 * FM_FPT - 1) / (256 * FM_FPT)); \
+    const dim3 grid(static_cast<unsigned>(rb), (feature_count(D, NT) + FM_FB - 1) / FM_FB);               \
     if (bf16)                                                                                          \
       hipLaunchKernelGGL((feature_map_kernel<D, NT, true>), grid, dim3(256), 0, stream, x, rows, phi, sc); \
     else                                                                                               \
