@@ -33,9 +33,9 @@
 // over the waves as fp32 accumulators: seven waves hold 9 pair-class tiles
 // each, grouped so that one wave's tiles share their first coordinate range
 // (at most two such groups per wave); wave 3 holds the linear, constant and
-// Gram tiles, the key sum z1 and the diagonal block (scores, weights, causal
-// mask, P V). Per 32-token chunk every wave reads its tiles
-// out into a partial output, then updates them. Partial outputs meet in
+// Gram tiles and the diagonal block (scores, weights, causal mask, P V),
+// wave 1 the key sum z1. Per 32-token chunk every wave reads its tiles out
+// into a partial output, then updates them. Partial outputs meet in
 // double-buffered LDS, and waves 0..3 normalise and store the previous chunk.
 //
 // Feature fragments. Key side (update, fp16 MFMA): packed fp16 products of
@@ -70,7 +70,8 @@ constexpr int C = 32;                     // tokens per chunk
 constexpr int NW = 8, NTHR = NW * 64;
 constexpr int F = 2145;
 constexpr int NS = 68, NZ = 3, NSLOT = NS + NZ;
-constexpr int W_AUX = 3;                  // linear, constant and Gram slots, z1, diagonal block
+constexpr int W_AUX = 3;                  // linear, constant and Gram slots, diagonal block
+constexpr int W_Z1 = 1;                   // key sum z1 and its read-out (1% faster than on W_AUX)
 constexpr float kSqrt2 = 1.41421356237309515f;
 
 enum { S_CLASS = 0, S_LIN = 1, S_CONST = 2, S_Z = 3 };
@@ -92,7 +93,7 @@ __host__ __device__ constexpr Slot slot_info(int s) {
 // Slots of each wave. Pair classes of one first-coordinate range (abase)
 // and consecutive offsets K stay together, so a wave's query features come
 // from at most two register blocks. The auxiliary wave (linear, constant
-// and Gram tiles, z1, diagonal block) also takes two pair classes: per chunk
+// and Gram tiles, diagonal block) also takes two pair classes: per chunk
 // it then issues about as many VALU instructions as a wave of nine classes,
 // but its work has more dependent steps. Waves w and w + 4 share a SIMD and
 // the older one (w < 4) gets issue priority. With the auxiliary slots on
@@ -571,7 +572,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
         }
       });
     }
-    if constexpr (W == W_AUX) {
+    if constexpr (W == W_Z1) {
       // linear part of the denominator, (q . z1) / a with z1 of the earlier
       // chunks (every row of the product equals q . z1), then z1 += keys
       if (out) {
@@ -594,6 +595,8 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
         for (int e = 0; e < 4; ++e) zs = __builtin_amdgcn_fdot2(f16x2{x[2 * e], x[2 * e + 1]}, ones, zs, false);
       }
       z1r += zs;
+    }
+    if constexpr (W == W_AUX) {
       if (out) {
         // diagonal block: scores D[key][query] = K Q^T (raw), weights,
         // causal mask, then O^T += V^T P^T with keys in the accumulator order
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
     f32x16 acc[NSW];
 #pragma unroll
     for (int i = 0; i < NSW; ++i) acc[i] = f32x16{};
-    float z1r = 0.f;  // wave W_AUX: z1 of coordinate l
+    float z1r = 0.f;  // wave W_Z1: z1 of coordinate l
 
     // initial state: unit p
     if (from_unit) {
@@ -693,7 +696,7 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
           acc[i][4 * q4 + 2] = x.z;
           acc[i][4 * q4 + 3] = x.w;
         }
-      if (W == W_AUX) z1r = reinterpret_cast<const float*>(unit_at(p) + Z1_F4)[l];
+      if (W == W_Z1) z1r = reinterpret_cast<const float*>(unit_at(p) + Z1_F4)[l];
     }
 
     // chunk loop: iteration i stages chunk i+1, computes chunk i and
@@ -723,12 +726,12 @@ __global__ __launch_bounds__(NTHR, 1) void w2_kernel(PrefillArgs a) {
         for (int q4 = 0; q4 < 4; ++q4)
           dstu[(SL.s[sl] * 4 + q4) * 64 + l] =
               float4{acc[sl][4 * q4], acc[sl][4 * q4 + 1], acc[sl][4 * q4 + 2], acc[sl][4 * q4 + 3]};
-      if (W == W_AUX) {
+      if (W == W_Z1) {
         reinterpret_cast<float*>(dstu + Z1_F4)[l] = z1r;
         if (l == 0) dstu[Z0_F4] = float4{count, 0.f, 0.f, 0.f};
       }
     } else if (want_state) {
-      if (W == W_AUX && hv == 0) {
+      if (W == W_Z1 && hv == 0) {
         float* z = a.z + static_cast<size_t>(bh) * F;
         z[1 + l] = z1r;
         if (l == 0) z[0] = count;
