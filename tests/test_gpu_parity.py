@@ -4,6 +4,7 @@ Tolerances: normwise relative error per head (max over heads) 1e-4 for fp32
 inputs and 2e-2 for bf16 inputs with fp32 accumulation, and a per-row bound
 on every checked row (tests/helpers.py).
 """
+import ctypes
 import math
 import sys
 
@@ -67,6 +68,28 @@ def test_feature_map(d, n, dtype, fold):
         g = to_f64(phi) @ to_f64(phi).T
         t = x["q64"][0, 0] @ x["q64"][0, 0].T / math.sqrt(d)
         assert np.max(np.abs(g - T.taylor_weight(t, n))) < 1e-4 * np.max(np.abs(g))
+
+
+@pytest.mark.parametrize("d,n", [(16, 3), (16, 5), (64, 3)])
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_feature_map_unaligned_output(d, n, offset):
+    # the output pointer 4, 8 or 12 bytes past a 16-byte boundary: the kernel
+    # aligns its 16-byte stores to the pointer, and the floats around the
+    # output stay untouched; 70 rows (more than one 64-row block, ragged)
+    rows = 70
+    x = W.make_qkv(1, 1, rows, d, 16, "bf16", 13)
+    F = tl.feature_dim(d, n)
+    buf = torch.full((rows * F + 8,), 7.0, dtype=torch.float32, device="cuda")
+    xd = to_device(x["q"][0, 0], "bf16")
+    say("feature_map unaligned", d, n, offset)
+    tl.check(tl.lib().taylor_feature_map(ctypes.c_void_p(xd.data_ptr()), tl.TAYLOR_BF16, rows, d, n, 0.0, 0,
+                                         ctypes.c_void_p(buf.data_ptr() + 4 * offset), tl._stream()))
+    torch.cuda.synchronize()
+    out = buf.double().cpu().numpy()
+    ref = T.phi(x["q64"][0, 0], n).reshape(-1)
+    got = out[offset:offset + rows * F]
+    assert np.max(np.abs(got - ref)) / np.max(np.abs(ref)) < 2e-6
+    assert np.all(out[:offset] == 7.0) and np.all(out[offset + rows * F:] == 7.0)
 
 
 @pytest.mark.parametrize("d,dv,n", CONFIGS)
