@@ -840,10 +840,14 @@ __global__ __launch_bounds__(NTHR, 1) void w2_segsum_fs(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lc = l & 31, lh = l >> 5;
   const int PL = a.P - 1;
-  const int unit = blockIdx.x;
-  if (unit >= a.BH * 2 * PL) return;
-  const int bhf = unit / PL, p = unit - bhf * PL;
-  const int bh = bhf >> 1, f = bhf & 1;
+  // blocks of 16 workgroups: eight (head, segment) pairs with feature half 0,
+  // then the same eight with half 1, so that the two halves of a pair are 8
+  // apart in dispatch order (workgroups go to the 8 XCDs round-robin) and
+  // share an L2 for the keys and values they both read
+  const int grp = blockIdx.x >> 4, r16 = blockIdx.x & 15;
+  const int f = r16 >> 3, hs = 8 * grp + (r16 & 7);  // (head, segment) index
+  if (hs >= a.BH * PL) return;
+  const int bh = hs / PL, p = hs - bh * PL;
   const int N = a.N;
   const int t0 = p * a.L;
   const int t1 = min(N, t0 + a.L);
@@ -1154,7 +1158,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (a.P > 1) {
-    hipLaunchKernelGGL(w2_segsum_fs, dim3(a.BH * 2 * (a.P - 1)), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL(w2_segsum_fs, dim3(16 * ((a.BH * (a.P - 1) + 7) / 8)), dim3(NTHR), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t n = static_cast<int64_t>(a.BH) * 2 * UNIT_F4;
     hipLaunchKernelGGL(w2_scan, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, seg, a.BH * 2,
