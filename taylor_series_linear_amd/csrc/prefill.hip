@@ -905,6 +905,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   constexpr int QB = MAIN ? NQI : 0;       // Q items exist only when reading out
   constexpr int NIT = QB + NQI + NVI;
   constexpr int NSLOT = (NIT + Cfg::NTHR - 1) / Cfg::NTHR;
+  static_assert(QB % 64 == 0 && NQI % 64 == 0 && NIT % 64 == 0, "staging items: whole waves per kind");
   uint4 pf[NSLOT];
 
   // Buffer resources over this segment's rows (base and size in scalar
@@ -912,9 +913,11 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   // as zero without branches.
   // (queries from t0, keys and values from the first token of the loop)
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0), loop_rows = static_cast<uint32_t>(t1 - lo);
-  const auto rq = make_rsrc(qh + static_cast<size_t>(t0) * D, want_out ? seg_rows * D * Cfg::ES : 0u);
-  const auto rk = make_rsrc(kh + static_cast<size_t>(lo) * D, loop_rows * D * Cfg::ES);
-  const auto rv = make_rsrc(vh + static_cast<size_t>(lo) * DV, loop_rows * DV * Cfg::ES);
+  const E* const qb = qh + static_cast<size_t>(t0) * D;
+  const E* const kb = kh + static_cast<size_t>(lo) * D;
+  const E* const vb = vh + static_cast<size_t>(lo) * DV;
+  const uint32_t qbytes = want_out ? seg_rows * D * Cfg::ES : 0u, kbytes = loop_rows * D * Cfg::ES,
+                 vbytes = loop_rows * DV * Cfg::ES;
   // V items (16 bytes each). V is written transposed, one element per
   // store: in wide slices consecutive lanes take consecutive rows (tokens)
   // of one 16-byte column group, so that the stores of a wave spread over
@@ -927,24 +930,43 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
   auto fetch = [&](int cc0) {
     const uint32_t r0 = static_cast<uint32_t>(cc0 - lo);
     const bool qrows = cc0 >= t0;  // prefix-pass chunks read no queries
+    constexpr uint32_t kNone = 0x7ffffff0u;  // past every buffer range: loads zeros
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int i = tid + s * Cfg::NTHR;
-      pf[s] = uint4{0, 0, 0, 0};
-      if (i < QB) {
+      // Every thread issues exactly one load per slot, straight into pf[s];
+      // items it does not have read zeros from past the range. (With
+      // conditional loads the compiler merged the loaded value into pf under
+      // an exec mask and waited for the load at once, stalling each loading
+      // wave for the load's latency.) The item kind is the same on all lanes
+      // of a wave (its boundaries are multiples of 64), so the buffer base
+      // and size are chosen in scalar registers.
+      const int kind = __builtin_amdgcn_readfirstlane(i < QB ? 0 : (i < QB + NQI ? 1 : (i < NIT ? 2 : 3)));
+      const E* bp = kb;
+      uint32_t nb = 0u, off = kNone;
+      if (kind == 0) {
         const int row = i / (D / EV), col = (i % (D / EV)) * EV;
-        if (qrows) pf[s] = bload16(rq, ((static_cast<uint32_t>(cc0 - t0) + row) * D + col) * Cfg::ES);
-      } else if (i < QB + NQI) {
+        bp = qb;
+        nb = qrows ? qbytes : 0u;
+        off = ((static_cast<uint32_t>(cc0 - t0) + row) * D + col) * Cfg::ES;
+      } else if (kind == 1) {
         const int j = i - QB;
         const int row = j / (D / EV), col = (j % (D / EV)) * EV;
-        pf[s] = bload16(rk, ((r0 + row) * D + col) * Cfg::ES);
-      } else if (i < NIT) {
+        nb = kbytes;
+        off = ((r0 + row) * D + col) * Cfg::ES;
+      } else if (kind == 2) {
         const int j = i - QB - NQI;
         const int row = v_row(j), col = v_col(j);
-        pf[s] = bload16(rv, ((r0 + row) * DV + col) * Cfg::ES);
+        bp = vb;
+        nb = vbytes;
+        off = ((r0 + row) * DV + col) * Cfg::ES;
       }
+      pf[s] = bload16(make_rsrc(bp, nb), off);
     }
   };
+
+
+
   // Q, K row-major (and, for the table-driven generator, transposed into the
   // coordinate rows of the factor tables); V transposed (key-contiguous) with
   // the ones row below it. Extended kernels first preprocess the Q and K
