@@ -497,24 +497,27 @@ __device__ __forceinline__ float state_scale(int f) {
 
 // Pair rows of both tables from their coordinate rows (rows 1..D, written
 // while staging): T[pair(i,j)][t] = T[1+i][t] T[1+j][t], 16 bytes at a time.
-// Thread tid handles pairs tid, tid + NTHR, ... of the 2 * NPAIR (query
-// pairs first); their coordinates are decoded once per kernel.
+// Thread tid handles pairs tid, tid + NTHR, ... of the query pairs and then
+// the key pairs (key pairs only with per-token query features), so the jobs
+// sit on the first waves, which have issue priority on their SIMDs; their
+// coordinates are decoded once per kernel.
 template <class Cfg>
 struct PairJobs {
   static constexpr int NPAIR = Cfg::D * (Cfg::D + 1) / 2;
-  static constexpr int N = Cfg::PAIRS ? (2 * NPAIR + Cfg::NTHR - 1) / Cfg::NTHR : 0;
+  static constexpr int NQP = Cfg::QGEN ? 0 : NPAIR;  // query-side pair jobs
+  static constexpr int N = Cfg::PAIRS ? (NQP + NPAIR + Cfg::NTHR - 1) / Cfg::NTHR : 0;
   int ij[N > 0 ? N : 1];  // i | j << 8, or -1
 };
 template <class Cfg>
 __device__ __forceinline__ PairJobs<Cfg> pair_jobs(int tid) {
-  constexpr int D = Cfg::D, NPAIR = PairJobs<Cfg>::NPAIR;
+  constexpr int D = Cfg::D, NPAIR = PairJobs<Cfg>::NPAIR, NQP = PairJobs<Cfg>::NQP;
   PairJobs<Cfg> pj;
 #pragma unroll
   for (int n = 0; n < PairJobs<Cfg>::N; ++n) {
     const int k = tid + n * Cfg::NTHR;
     pj.ij[n] = -1;
-    if (k < 2 * NPAIR) {
-      int r = k < NPAIR ? k : k - NPAIR, pi = 0;
+    if (k < NQP + NPAIR) {
+      int r = k < NQP ? k : k - NQP, pi = 0;
       while (r >= D - pi) {
         r -= D - pi;
         ++pi;
@@ -527,14 +530,14 @@ __device__ __forceinline__ PairJobs<Cfg> pair_jobs(int tid) {
 template <class Cfg, class KE>
 __device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, float* __restrict__ TQ,
                                             KE* __restrict__ TK, bool qside) {
-  constexpr int D = Cfg::D, C = Cfg::C, NPAIR = PairJobs<Cfg>::NPAIR;
+  constexpr int D = Cfg::D, C = Cfg::C, NQP = PairJobs<Cfg>::NQP;
 #pragma unroll
   for (int n = 0; n < PairJobs<Cfg>::N; ++n) {
     const int k = tid + n * Cfg::NTHR;
     const int ij = pj.ij[n];
     if (ij < 0) continue;
     const int pi = ij & 255, pjj = ij >> 8;
-    if (k < NPAIR) {
+    if (k < NQP) {
       if (!qside) continue;
       const f32x4* xi = reinterpret_cast<const f32x4*>(TQ + (1 + pi) * Cfg::TP);
       const f32x4* xj = reinterpret_cast<const f32x4*>(TQ + (1 + pjj) * Cfg::TP);
@@ -575,16 +578,18 @@ __device__ __forceinline__ void build_pairs(int tid, const PairJobs<Cfg>& pj, fl
 
 // Blocks of 64 features of the table-driven generators, per wave: entry j
 // of wave w is block w + NW j, except that when the blocks beyond one per
-// wave (R of them, fewer than the waves) divide the waves, each of them is
-// split by tokens over NW / R waves, so that every wave does the same work
-// (a 640-feature slice on eight waves: one block and a quarter of one).
+// wave (R of them) divide the first half of the waves, each of them is split
+// by tokens over NW / (2 R) of those waves (a 640-feature slice on eight
+// waves: one block each, and half a block more on waves 0..3). Waves w and
+// w + 4 share a SIMD and the older one, w < 4, gets issue priority: the same
+// work takes longer on waves 4..7, so the first half takes the extra.
 template <class Cfg>
 struct TabSplit {
-  static constexpr int NB = (Cfg::FS + 63) / 64, NW = Cfg::NW, R = NB - NW;
-  static constexpr bool BAL = R > 0 && R < NW && NW % R == 0 && (Cfg::C / (NW / R)) % 8 == 0;
-  static constexpr int P = BAL ? NW / R : 1;     // token pieces per left-over block
+  static constexpr int NB = (Cfg::FS + 63) / 64, NW = Cfg::NW, R = NB - NW, HW = NW / 2;
+  static constexpr bool BAL = R > 0 && R <= HW && HW % R == 0 && (Cfg::C / (HW / R)) % 8 == 0;
+  static constexpr int P = BAL ? HW / R : 1;     // token pieces per left-over block
   static constexpr int NBW = (NB + NW - 1) / NW;  // entries per wave
-  __device__ static int block(int w, int j) { return BAL ? (j == 0 ? w : NW + w / P) : w + NW * j; }
+  __device__ static int block(int w, int j) { return BAL ? (j == 0 ? w : (w < HW ? NW + w / P : NB)) : w + NW * j; }
   __device__ static int tok0(int w, int j) { return BAL && j > 0 ? (w % P) * (Cfg::C / P) : 0; }
   template <int J>
   static constexpr int ntok() { return BAL && J > 0 ? Cfg::C / P : Cfg::C; }
