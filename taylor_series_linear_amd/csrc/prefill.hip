@@ -1231,7 +1231,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void prefill_kernel(PrefillArgs a) {
               *reinterpret_cast<f32x4*>(pr + col) = o;
               if (col == 0) pr[DV] = dsum;
             }
-          }        } else {
+          }
+        } else {
           // feature groups 1 .. NFG-1 hand their value partials to group 0,
           // every wave its share of the denominator
           if (fg > 0) {
